@@ -1,0 +1,343 @@
+"""CPU oracle for the DSA lightning-indexer hot path (TEST INFRASTRUCTURE ONLY).
+
+This module is the slow, plain, obviously-correct definition that the HIP path is
+checked against.  Only the test suite, the smoke check and the CPU-baseline leg of
+the benchmark may import it; the product library never does, and it shares no
+code, tables or constants with the HIP sources.
+
+Everything floating point is computed in float64 on exactly-decoded inputs, except
+the fp8 quantiser, whose output is a set of integer codes and is therefore specified
+in float32 (see ``quant_fp8``).
+
+Sources (web pages; cited by title and section):
+  [ATOM-1507]  "[DeepSeek-V4] index_topk=1024 sparse indexer can't recall verbatim
+               lines from ~18k+ prompts" (ROCm/ATOM issue 1507)
+  [PIVOT-DIAG] "The Pivot: Diagnosing a Sparse Attention Recall Bug at the
+               Intersection of Precision and Production"
+  [PIVOT-EDIT] "The Pivot: A Single Edit That Finally Fixed DeepSeek V4's
+               Long-Context Recall Failure"
+  [HYPOTHESIS] "The Hypothesis That Refused to Die: When Synthetic Tests
+               Contradict Real-World Failure"
+
+Readings where the pages are silent are marked READING and are the plainest ones
+the rest of the pages support.
+
+Pin status of every public function (what fixes it other than itself is in
+tests/test_oracle_*.py):
+  e4m3_decode, e4m3_encode, quant_fp8 ..... pinned (format definition values,
+                                             torch float8_e4m3fn, exact rationals)
+  hadamard_matrix, rmsnorm, rope,
+  store_chain ............................. pinned (closed forms, invariants,
+                                             scipy.linalg.hadamard)
+  score, score_rows ....................... pinned (exact-rational brute force,
+                                             closed forms, invariants)
+  topk ..................................... pinned (subset brute force, numpy and
+                                             torch library routines)
+  jaccard .................................. pinned (the printed table of the
+                                             synthetic fp8-vs-bf16 test)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+HEAD_DIM = 128
+E4M3_MAX = 448.0
+
+# ----------------------------------------------------------------------------------
+# bf16 / fp32 helpers (exact conversions only)
+# ----------------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+# ----------------------------------------------------------------------------------
+# OCP FP8 E4M3 (e4m3fn): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits, no
+# infinities, NaN = S.1111.111.  The pages only say the index keys are "e4m3" fp8
+# with three mantissa bits ([HYPOTHESIS], "Input Knowledge Required", item 3) and a
+# per-token fp32 scale, 132 bytes per token ([PIVOT-EDIT], "Assumptions and Input
+# Knowledge").  READING: the OCP e4m3fn flavour, which is the native fp8 of the
+# target GPU; largest finite magnitude 448.
+# ----------------------------------------------------------------------------------
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each e4m3fn code as float64 (NaN for 0x7F / 0xFF).
+
+    Normal codes (exponent field e > 0): (-1)^s * 2^(e-7) * (1 + m/8).
+    Subnormal codes (e == 0):            (-1)^s * 2^(-6) * (m/8).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def _e4m3_positive_table() -> np.ndarray:
+    """The 127 finite non-negative e4m3 values, indexed by code 0x00..0x7E."""
+    return e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round float32 values to e4m3fn codes: nearest finite value, ties to the code
+    with an even mantissa (round-to-nearest-even), saturating to +-448, keeping the
+    sign (so -0 and negative underflow give 0x80).
+
+    READING (quantiser rounding): round-to-nearest-even with saturation.  Under
+    absmax scaling saturation is never reached except through the all-zero rule.
+
+    The comparison is exact: every float32 and every e4m3 midpoint is exactly
+    representable in float64, and the value is compared with the midpoint of its two
+    neighbouring codes rather than with a difference that could round.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    if np.isnan(x32).any():
+        raise ValueError("e4m3_encode: NaN input")
+    sign = (x32.view(np.uint32) >> np.uint32(31)).astype(np.uint8)
+    a = np.abs(x32.astype(np.float64))
+    table = _e4m3_positive_table()                 # ascending, codes 0..126
+    hi = np.searchsorted(table, a, side="left")    # first table value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    v_lo, v_hi = table[lo], table[hi]
+    mid = (v_lo + v_hi) / 2.0                      # exact (dyadic, few bits)
+    exact_hit = v_hi == a
+    pick_hi = (a > mid) | ((a == mid) & (hi % 2 == 0))
+    code = np.where(exact_hit, hi, np.where(pick_hi, hi, lo))
+    code = np.where(a >= E4M3_MAX, 126, code)      # saturate (satfinite)
+    return (code.astype(np.uint8) | (sign << np.uint8(7))).astype(np.uint8)
+
+
+def quant_fp8(x) -> tuple[np.ndarray, np.ndarray]:
+    """Per-vector absmax fp8 quantisation of rows of 128 values.
+
+    The pages store each index key as 128 e4m3 codes plus one fp32 scale (132 B per
+    token, [PIVOT-EDIT] "Assumptions and Input Knowledge"); write, read and scale are
+    each checked with zero error ([ATOM-1507] "How it was isolated").  They do not
+    print the quantiser.  READING (the plainest per-token absmax form):
+        amax = max_i |x_i|                      (float32, exact)
+        s    = fl32(amax / 448)                 (correctly rounded fp32 division)
+        c_i  = e4m3_encode(fl32(x_i / s))       (correctly rounded fp32 division)
+    and, for an all-zero (or vanishingly small, amax < 2^-100) vector, s = 1, which
+    yields all-zero codes.  Dequantised value: s * decode(c_i).
+
+    Input: float32-representable values, shape [..., 128].  Returns (codes uint8
+    [..., 128], scales float32 [...]).
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(amax < np.float32(2.0 ** -100), np.float32(1.0), s).astype(np.float32)
+    y = (x32 / s[..., None]).astype(np.float32)
+    return e4m3_encode(y), s
+
+
+def dequant_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 value of quantised vectors: scale * decode(code), exact."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+# ----------------------------------------------------------------------------------
+# Index-K store chain: RMSNorm -> RoPE -> Hadamard -> (quantise) -> paged write.
+# Order from [PIVOT-EDIT] "The Reasoning Behind the Edit" (normalisation, RoPE and
+# rotation as separate steps before storing) and [ATOM-1507] "Where" (interleaved
+# RoPE on the trailing rope_dim, then the Walsh-Hadamard rotation).
+# ----------------------------------------------------------------------------------
+
+STORE_RMSNORM = 1
+STORE_ROPE = 2
+STORE_HADAMARD = 4
+
+
+def hadamard_matrix(n: int = HEAD_DIM) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard matrix in Sylvester (natural) order, by the
+    recursion H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]].  Integer entries +-1.
+
+    [ATOM-1507] "Root cause found": H is orthogonal, so (Hq).(Hk) = q.k once it is
+    normalised by 1/sqrt(n).  READING: natural (Sylvester) order.
+    """
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    h = np.ones((1, 1), dtype=np.int64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def rmsnorm(x: np.ndarray, eps: float) -> np.ndarray:
+    """y = x / sqrt(mean(x^2) + eps), unit gain, float64.
+
+    [PIVOT-EDIT] "The Reasoning Behind the Edit" names normalisation as the first
+    store step; READING: RMS normalisation with unit gain (the gain is a trained
+    weight the pages do not give) and eps a parameter.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rope(x: np.ndarray, positions: np.ndarray, base: float, rope_dim: int) -> np.ndarray:
+    """Interleaved rotary embedding on the trailing rope_dim dimensions, float64.
+
+    With o = 128 - rope_dim, pair i = (x[o+2i], x[o+2i+1]) is rotated by the angle
+    theta_i = pos * base^(-2i/rope_dim):
+        x'[o+2i]   = x[o+2i] cos(theta_i) - x[o+2i+1] sin(theta_i)
+        x'[o+2i+1] = x[o+2i] sin(theta_i) + x[o+2i+1] cos(theta_i)
+    Dimensions below o are untouched.  ([ATOM-1507] "Where": "interleaved RoPE to
+    trailing rope_dim".)  The angle is formed in float64; positions reach ~1M.
+    """
+    x = np.array(x, dtype=np.float64, copy=True)
+    d = x.shape[-1]
+    if rope_dim % 2 or not (2 <= rope_dim <= d):
+        raise ValueError("rope_dim must be even and in [2, head_dim]")
+    o = d - rope_dim
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    inv_freq = np.power(float(base), -2.0 * i / rope_dim)            # [rope_dim/2]
+    theta = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    c, s = np.cos(theta), np.sin(theta)
+    a = x[:, o::2].copy()
+    b = x[:, o + 1::2].copy()
+    x[:, o::2] = a * c - b * s
+    x[:, o + 1::2] = a * s + b * c
+    return x
+
+
+def store_chain(x_bits: np.ndarray, positions: np.ndarray, flags: int, eps: float,
+                base: float, rope_dim: int) -> np.ndarray:
+    """float64 pre-quantisation rows of the index-K store: decoded bf16 input, then
+    (optionally) RMSNorm, RoPE and the normalised Hadamard rotation y = H x / sqrt(128),
+    in that order.  Returns float64 [n, 128]."""
+    y = bf16_bits_to_f64(x_bits)
+    if flags & STORE_RMSNORM:
+        y = rmsnorm(y, eps)
+    if flags & STORE_ROPE:
+        y = rope(y, positions, base, rope_dim)
+    if flags & STORE_HADAMARD:
+        h = hadamard_matrix(y.shape[-1]).astype(np.float64)
+        y = (y @ h.T) / np.sqrt(float(y.shape[-1]))
+    return y
+
+
+# ----------------------------------------------------------------------------------
+# Indexer score
+# ----------------------------------------------------------------------------------
+
+
+def score(q: np.ndarray, w: np.ndarray, keys: np.ndarray, row_len: int | None = None) -> np.ndarray:
+    """Relevance score of every visible key for one query row, float64.
+
+        o[p] = sum_h w[h] * max(0, sum_d q[h, d] * k[p, d])   for p < row_len
+
+    The pages name the parts: a query-key dot product per index head ([ATOM-1507]
+    "Root cause found", [HYPOTHESIS] "The Context": a compressed query-key dot
+    product), a per-head weights projection and a softmax scaling ([HYPOTHESIS]
+    "The Bash Command").  READING: ReLU of each head's logit, weighted by w_h and
+    summed over heads; any positive global scale is folded into w (it cannot change
+    a top-k since ReLU(cx) = c ReLU(x) for c > 0).  Keys at p >= row_len are never
+    read (causal / committed-key mask).
+
+    q: [H, 128], w: [H], keys: [L, 128] (already dequantised, float64).
+    Returns float64 [row_len].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    n = keys.shape[0] if row_len is None else int(row_len)
+    if n == 0:
+        return np.zeros(0, dtype=np.float64)
+    k = np.asarray(keys[:n], dtype=np.float64)
+    logits = q @ k.T                                   # [H, n]
+    return w @ np.maximum(logits, 0.0)                 # [n]
+
+
+def score_rows(q: np.ndarray, w: np.ndarray, seq_keys, row_seq, row_len,
+               max_row_len: int, chunk: int = 1 << 16) -> np.ndarray:
+    """Scores of many rows laid out as a [rows, max_row_len] float64 matrix with
+    -inf at masked positions (p >= row_len[r]).
+
+    q: [rows, H, 128]; w: [rows, H]; seq_keys: sequence -> float64 keys [L_b, 128]
+    (a list, or a callable taking (b, start, stop)).  Keys are consumed in chunks so
+    long rows stay within memory; chunking only splits the sum over keys, not the
+    sum over heads or dimensions, so it changes nothing.
+    """
+    rows = len(row_len)
+    out = np.full((rows, max_row_len), -np.inf, dtype=np.float64)
+    for r in range(rows):
+        b, n = int(row_seq[r]), int(row_len[r])
+        for p0 in range(0, n, chunk):
+            p1 = min(n, p0 + chunk)
+            k = seq_keys(b, p0, p1) if callable(seq_keys) else seq_keys[b][p0:p1]
+            out[r, p0:p1] = score(q[r], w[r], k)
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# Top-k selection
+# ----------------------------------------------------------------------------------
+
+
+def topk(scores: np.ndarray, row_len, k: int) -> np.ndarray:
+    """Causal top-k per row.
+
+    For row r only positions p < row_len[r] are candidates.  They are ordered by
+    score descending, ties broken by the lower position, and the first
+    min(k, row_len[r]) are kept.  READING (output form): the kept positions are
+    returned in ascending order and the row is padded with -1 to length k.  Zero
+    scores of either sign compare equal (they are the same number).
+
+    ([ATOM-1507] "Summary"/"How it was isolated": index_topk of 512 or 1024 kept
+    per row; the selection kernel is judged by overlap with torch.topk.)
+    """
+    scores = np.asarray(scores)
+    rows = scores.shape[0]
+    out = np.full((rows, k), -1, dtype=np.int32)
+    for r in range(rows):
+        n = int(row_len[r])
+        if n <= 0:
+            continue
+        s = scores[r, :n].astype(np.float64)
+        order = np.argsort(-s, kind="stable")          # stable: lower index first on ties
+        keep = np.sort(order[:min(k, n)])
+        out[r, :keep.size] = keep
+    return out
+
+
+def kth_score(scores_row: np.ndarray, n: int, k: int) -> float:
+    """The k-th largest visible score of a row (the selection threshold tau)."""
+    s = np.sort(np.asarray(scores_row[:n], dtype=np.float64))[::-1]
+    return float(s[min(k, n) - 1])
+
+
+def rank_of(scores_row: np.ndarray, n: int, p: int) -> int:
+    """1-based rank of position p under (score desc, position asc)."""
+    s = np.asarray(scores_row[:n], dtype=np.float64)
+    return int(np.sum(s > s[p]) + np.sum(s[:p] == s[p]) + 1)
+
+
+# ----------------------------------------------------------------------------------
+# fp8-vs-bf16 selection overlap
+# ----------------------------------------------------------------------------------
+
+
+def jaccard(a, b) -> tuple[float, int]:
+    """Jaccard overlap |A n B| / |A u B| of two selections and the number of
+    positions of A missing from B (|A \\ B|), -1 padding ignored.
+
+    ([HYPOTHESIS] "Message 12994: The Synthetic Test": "jacc512" and
+    "lost(bf16->fp8)" columns, with A the bf16-key selection and B the fp8-key one.)
+    """
+    sa = {int(v) for v in np.asarray(a).ravel() if v >= 0}
+    sb = {int(v) for v in np.asarray(b).ravel() if v >= 0}
+    union = sa | sb
+    if not union:
+        return 1.0, 0
+    return len(sa & sb) / len(union), len(sa - sb)
