@@ -1,0 +1,218 @@
+/*
+ * dsa_indexer.h - C ABI of the DeepSeek sparse-attention (DSA) lightning-indexer hot
+ * path on AMD Instinct MI355X (gfx950): index-K store, per-key relevance score and
+ * causal top-k over a paged index-K cache.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [ATOM-1507]  "[DeepSeek-V4] index_topk=1024 sparse indexer can't recall verbatim
+ *                lines from ~18k+ prompts" (ROCm/ATOM issue 1507)
+ *   [PIVOT-EDIT] "The Pivot: A Single Edit That Finally Fixed DeepSeek V4's
+ *                Long-Context Recall Failure"
+ *   [HYPOTHESIS] "The Hypothesis That Refused to Die: When Synthetic Tests
+ *                Contradict Real-World Failure"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as device buffers are device pointers owned by the caller.  The
+ *    library never allocates or frees device memory, never synchronises a stream and
+ *    never reads device data on the host.  Scratch space is the caller's `ws`.
+ *  - All work is queued on `hip_stream` (a hipStream_t; NULL = the null stream) and
+ *    is asynchronous.  No call records a memset, so calls can be captured in a HIP
+ *    graph.
+ *  - Errors: argument checks run on the host before anything is launched; on failure
+ *    the call returns IDX_EINVAL / IDX_EUNSUPPORTED / IDX_EWORKSPACE, launches
+ *    nothing and sets a message readable with indexer_last_error() (thread-local).
+ *    A failed launch returns IDX_ELAUNCH.  Nothing throws across the ABI.
+ *  - Device-resident indices (block ids, slots, positions, row lengths, row
+ *    sequences) cannot be checked on the host.  The kernels never access memory out
+ *    of bounds because of them: a block id outside [0, num_blocks) scores NaN, a
+ *    store slot outside the pool is skipped, row_len is clamped to
+ *    [0, max_row_len] and a row_seq outside [0, num_seqs) scores NaN.
+ *  - head_dim is 128 throughout.  Outputs are bit-deterministic: there are no
+ *    floating-point atomics.
+ *  - Calls are re-entrant; the only global state is the thread-local error string.
+ */
+#ifndef DSA_INDEXER_H
+#define DSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IDX_ABI_VERSION 1
+#define IDX_HEAD_DIM 128
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_EINVAL = -1,        /* bad argument (null pointer, size, alignment, range) */
+  IDX_EUNSUPPORTED = -2,  /* valid but unsupported combination (dtype pair, heads) */
+  IDX_ELAUNCH = -3,       /* kernel launch failed (HIP error) */
+  IDX_EWORKSPACE = -4     /* workspace missing or smaller than required */
+} idx_status;
+
+typedef enum { IDX_BF16 = 1, IDX_FP8_E4M3 = 2 } idx_dtype;
+
+/* index_k_store flags: which steps precede the quantise-and-scatter.  flags = 0
+ * stores the input as given (quantised for an fp8 cache). */
+enum { IDX_STORE_RMSNORM = 1u, IDX_STORE_ROPE = 2u, IDX_STORE_HADAMARD = 4u };
+
+/* ops for indexer_workspace_bytes */
+enum { IDX_OP_TOPK = 1, IDX_OP_SCORE_TOPK = 2 };
+
+/*
+ * Paged index-K cache ([ATOM-1507] "How it was isolated": paged index-K cache read
+ * through a block table at block size 32 or 64; [PIVOT-EDIT] "Assumptions and Input
+ * Knowledge": 132 bytes per token for fp8, 256 for bf16).
+ *   base        device pointer to block 0, 256-byte aligned.
+ *   dtype       IDX_BF16: block b holds block_size rows of 128 bf16 (256 B each),
+ *                 at base + b*block_size*256.
+ *               IDX_FP8_E4M3: block b is block_size*132 bytes at
+ *                 base + b*block_size*132: first block_size*128 bytes of OCP e4m3fn
+ *                 codes (row-major, 128 per token), then block_size fp32 scales.
+ *                 Token value = scale * decode(code).
+ *   block_size  tokens per block: 32 or 64.
+ *   num_blocks  blocks in the pool (physical block ids are in [0, num_blocks)).
+ */
+typedef struct {
+  void* base;
+  int32_t dtype;
+  int32_t block_size;
+  int64_t num_blocks;
+} idx_kcache;
+
+/*
+ * Query rows and what each row may see (causal / committed-key mask, [ATOM-1507]
+ * "Analysis / question" and "How it was isolated").
+ *   block_table  device int32 [num_seqs][max_blocks]: physical block of each
+ *                logical block of each sequence.
+ *   row_seq      device int32 [rows]: the sequence a query row reads.
+ *   row_len      device int32 [rows]: row r sees key positions 0..row_len[r]-1
+ *                (its own key included, stored before scoring).
+ *   max_row_len  host-known upper bound of every row_len (sizes the grid and the
+ *                score rows); must be <= max_blocks*block_size.
+ */
+typedef struct {
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  const int32_t* row_seq;
+  const int32_t* row_len;
+  int32_t rows;
+  int32_t max_row_len;
+} idx_rows;
+
+/*
+ * index_k_store - write n index keys into the paged cache.
+ * Steps ([PIVOT-EDIT] "The Reasoning Behind the Edit": normalise, RoPE, rotate, then
+ * store; [ATOM-1507] "Root cause found"/"Where": interleaved RoPE on the trailing
+ * rope_dim, then the Walsh-Hadamard rotation that must match the query's; the
+ * store is the analog of the pages' indexer_k_quant_and_cache / fused compressor
+ * store), each enabled by a flag:
+ *   RMSNorm   y = x / sqrt(mean(x^2) + rms_eps), unit gain
+ *   RoPE      pair i = (y[o+2i], y[o+2i+1]), o = 128 - rope_dim, rotated by
+ *             pos * rope_base^(-2i/rope_dim) (angle formed in double precision)
+ *   Hadamard  y = H y / sqrt(128), H the 128x128 Sylvester-order Walsh matrix
+ *   store     fp8 cache: amax = max|y|, s = amax/448 (correctly rounded fp32
+ *             division; s = 1 when amax < 2^-100), code = e4m3(y/s) rounded to
+ *             nearest even with saturation; bf16 cache: y rounded to nearest even.
+ * Arguments:
+ *   x_bf16        device bf16 [n][128] hidden rows (row-major).
+ *   n             number of tokens (0 is a no-op).
+ *   positions     device int32 [n]: RoPE positions (read only with IDX_STORE_ROPE;
+ *                 may be NULL otherwise).
+ *   slot_mapping  device int64 [n]: destination slot = block*block_size + offset;
+ *                 a negative slot skips the token.
+ *   prequant_dbg  NULL, or device fp32 [n][128] receiving the rows just before
+ *                 quantisation / rounding (debug output).
+ *   rope_dim      even, 2..128 (read only with IDX_STORE_ROPE).
+ */
+int32_t index_k_store(const void* x_bf16, int64_t n, const int32_t* positions,
+                      const int64_t* slot_mapping, idx_kcache cache, uint32_t flags,
+                      float rms_eps, float rope_base, int32_t rope_dim, float* prequant_dbg,
+                      void* hip_stream);
+
+/*
+ * indexer_quant_fp8 - per-vector absmax fp8 quantisation of contiguous vectors of
+ * 128 values (the query-side fp8 step of the pages' rope_rotate_activation,
+ * [ATOM-1507] "Where"), with exactly the same rule as the fp8 store.
+ *   x_bf16  device bf16 [n_vec][128];  codes  device uint8 [n_vec][128];
+ *   scales  device fp32 [n_vec].
+ */
+int32_t indexer_quant_fp8(const void* x_bf16, int64_t n_vec, uint8_t* codes, float* scales,
+                          void* hip_stream);
+
+/*
+ * indexer_score - relevance of every visible cached key for every query row:
+ *     scores[r][p] = sum_h w[r][h] * max(0, q[r][h] . k[p])      for p < row_len[r]
+ *     scores[r][p] = -inf                         for row_len[r] <= p < max_row_len
+ * (the lightning-indexer q.k score, [ATOM-1507] "Root cause found"; a compressed
+ * query-key dot product, [HYPOTHESIS] "The Context"; per-head weights and a
+ * positive softmax scale, [HYPOTHESIS] "The Bash Command", folded into w).  An fp8
+ * key contributes scale_p * (q . decode(codes_p)); the per-key scale is applied
+ * after the head sum.  An fp8 query contributes q_scale[r][h] * decode(code).
+ * Zero scores are +0.
+ *   q        device [rows][heads][128]: bf16 (q_dtype IDX_BF16) or e4m3 codes
+ *            (IDX_FP8_E4M3, from indexer_quant_fp8).
+ *   q_scale  device fp32 [rows][heads] for fp8 q, else ignored (may be NULL).
+ *   w        device fp32 [rows][heads].
+ *   heads    64 (v1).
+ *   scores   device fp32 [rows][ld], ld >= max_row_len; columns >= max_row_len are
+ *            not written.
+ * Supported (q, key) dtypes: (bf16, bf16), (bf16, fp8), (fp8, fp8).
+ */
+int32_t indexer_score(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                      int32_t heads, idx_kcache cache, idx_rows rows, float* scores, int64_t ld,
+                      void* hip_stream);
+
+/*
+ * indexer_topk - causal top-k of score rows ([ATOM-1507] "Summary": index_topk 512
+ * or 1024; "How it was isolated": the per-row top-k is judged against torch.topk).
+ * Row r selects, among positions p < row_len[r], the k largest scores, ties broken
+ * by the lower position (+0 and -0 are equal).  out_idx[r] holds the selected
+ * positions in ascending order followed by -1 padding when row_len[r] < k.
+ * NaN scores give an unspecified (but in-bounds) selection.
+ *   scores   device fp32 [rows][ld];  row_len  device int32 [rows].
+ *   k        1..8192.
+ *   out_idx  device int32 [rows][k].
+ *   ws       device workspace of at least
+ *            indexer_workspace_bytes(IDX_OP_TOPK, rows, max_row_len, k) bytes,
+ *            256-byte aligned (NULL allowed when that size is 0).
+ */
+int32_t indexer_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t rows,
+                     int32_t max_row_len, int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes,
+                     void* hip_stream);
+
+/*
+ * indexer_score_topk - indexer_score followed by indexer_topk in one call (the
+ * pages' prefill orchestration and the decode selection, [ATOM-1507] "Recommended
+ * fix" and "How it was isolated").  Same arguments as the two calls; the scores
+ * live in the workspace.
+ *   out_idx     device int32 [rows][k] (as indexer_topk).
+ *   out_scores  NULL, or device fp32 [rows][k]: the score of each selected
+ *               position, -inf for padding.
+ *   ws          at least indexer_workspace_bytes(IDX_OP_SCORE_TOPK, rows,
+ *               max_row_len, k) bytes, 256-byte aligned.
+ */
+int32_t indexer_score_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                           int32_t heads, idx_kcache cache, idx_rows rows, int32_t k,
+                           int32_t* out_idx, float* out_scores, void* ws, size_t ws_bytes,
+                           void* hip_stream);
+
+/* Workspace bytes needed by an op (IDX_OP_TOPK or IDX_OP_SCORE_TOPK); 0 on bad
+ * arguments. */
+size_t indexer_workspace_bytes(int32_t op, int32_t rows, int32_t max_row_len, int32_t k);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* indexer_last_error(void);
+
+/* IDX_ABI_VERSION of the built library. */
+int32_t indexer_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEXER_H */

@@ -1,0 +1,218 @@
+"""Python binding of libdsa_indexer.so (the C ABI in include/dsa_indexer.h).
+
+Argument marshalling only: every step of the indexer runs in the library's HIP
+kernels.  Tensors are torch tensors on the current HIP device; work is queued on
+torch's current stream.  If the library has not been built the import fails loudly
+(there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")
+
+IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_ELAUNCH, IDX_EWORKSPACE = 0, -1, -2, -3, -4
+IDX_BF16, IDX_FP8_E4M3 = 1, 2
+IDX_STORE_RMSNORM, IDX_STORE_ROPE, IDX_STORE_HADAMARD = 1, 2, 4
+IDX_STORE_ALL = 7
+IDX_OP_TOPK, IDX_OP_SCORE_TOPK = 1, 2
+HEAD_DIM = 128
+
+EXPORTED = ("index_k_store", "indexer_quant_fp8", "indexer_score", "indexer_topk",
+            "indexer_score_topk", "indexer_workspace_bytes", "indexer_last_error",
+            "indexer_abi_version")
+
+
+class IndexerError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+class KCache(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int64)]
+
+
+class Rows(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("row_seq", ctypes.c_void_p),
+                ("row_len", ctypes.c_void_p), ("rows", ctypes.c_int32),
+                ("max_row_len", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and return the ctypes handle; raises if the library is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run `python -m sparse_attention_token_store_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                  ctypes.c_float, ctypes.c_size_t)
+    sig = {
+        "index_k_store": (i32, [vp, i64, vp, vp, KCache, u32, f32, f32, i32, vp, vp]),
+        "indexer_quant_fp8": (i32, [vp, i64, vp, vp, vp]),
+        "indexer_score": (i32, [vp, i32, vp, vp, i32, KCache, Rows, vp, i64, vp]),
+        "indexer_topk": (i32, [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]),
+        "indexer_score_topk": (i32, [vp, i32, vp, vp, i32, KCache, Rows, i32, vp, vp, vp, sz, vp]),
+        "indexer_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "indexer_last_error": (ctypes.c_char_p, []),
+        "indexer_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, code):
+    if code != IDX_OK:
+        raise IndexerError(fn, code, load_library().indexer_last_error().decode())
+
+
+def _need(t, dtype, name):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def kcache(buf, dtype: int, block_size: int, num_blocks: int) -> KCache:
+    """Describe a paged cache held in the uint8 device tensor `buf`."""
+    import torch
+    _need(buf, torch.uint8, "cache buffer")
+    per_block = block_size * (256 if dtype == IDX_BF16 else 132)
+    if buf.numel() < per_block * num_blocks:
+        raise ValueError("cache buffer smaller than num_blocks blocks")
+    return KCache(buf.data_ptr(), dtype, block_size, num_blocks)
+
+
+def cache_bytes(dtype: int, block_size: int, num_blocks: int) -> int:
+    return block_size * (256 if dtype == IDX_BF16 else 132) * num_blocks
+
+
+def rows_desc(block_table, row_seq, row_len, max_row_len: int) -> Rows:
+    import torch
+    for t, n in ((block_table, "block_table"), (row_seq, "row_seq"), (row_len, "row_len")):
+        _need(t, torch.int32, n)
+    return Rows(block_table.data_ptr(), block_table.shape[1], block_table.shape[0],
+                row_seq.data_ptr(), row_len.data_ptr(), row_len.shape[0], int(max_row_len))
+
+
+def workspace_bytes(op: int, rows: int, max_row_len: int, k: int) -> int:
+    return int(load_library().indexer_workspace_bytes(op, rows, max_row_len, k))
+
+
+def abi_version() -> int:
+    return int(load_library().indexer_abi_version())
+
+
+# ------------------------------------------------------------------ entry points
+
+def index_k_store(x, positions, slot_mapping, cache: KCache, flags: int = 0, rms_eps: float = 1e-6,
+                  rope_base: float = 10000.0, rope_dim: int = 64, prequant_dbg=None, stream=None):
+    import torch
+    _need(x, torch.bfloat16, "x")
+    _need(positions, torch.int32, "positions")
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    _need(prequant_dbg, torch.float32, "prequant_dbg")
+    n = x.shape[0]
+    if x.shape[-1] != HEAD_DIM or slot_mapping.shape[0] != n:
+        raise ValueError("x must be [n,128] and slot_mapping [n]")
+    _check("index_k_store", load_library().index_k_store(
+        _ptr(x), n, _ptr(positions), _ptr(slot_mapping), cache, flags, rms_eps, rope_base, rope_dim,
+        _ptr(prequant_dbg), _stream(stream)))
+
+
+def indexer_quant_fp8(x, codes, scales, stream=None):
+    import torch
+    _need(x, torch.bfloat16, "x")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float32, "scales")
+    n_vec = x.numel() // HEAD_DIM
+    if codes.numel() != x.numel() or scales.numel() != n_vec:
+        raise ValueError("codes must match x and scales must have x.numel()/128 entries")
+    _check("indexer_quant_fp8", load_library().indexer_quant_fp8(
+        _ptr(x), n_vec, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def _q_args(q, q_scale, w):
+    import torch
+    if q.dtype == torch.bfloat16:
+        q_dtype = IDX_BF16
+    elif q.dtype == torch.uint8:
+        q_dtype = IDX_FP8_E4M3
+        _need(q_scale, torch.float32, "q_scale")
+    else:
+        raise TypeError("q must be bf16 or uint8 e4m3 codes")
+    _need(q, q.dtype, "q")
+    _need(w, torch.float32, "w")
+    return q_dtype, q.shape[1]
+
+
+def indexer_score(q, w, cache: KCache, rows: Rows, scores, q_scale=None, stream=None):
+    import torch
+    q_dtype, heads = _q_args(q, q_scale, w)
+    _need(scores, torch.float32, "scores")
+    _check("indexer_score", load_library().indexer_score(
+        _ptr(q), q_dtype, _ptr(q_scale), _ptr(w), heads, cache, rows, _ptr(scores),
+        scores.shape[1], _stream(stream)))
+
+
+def indexer_topk(scores, row_len, max_row_len: int, k: int, out_idx, ws=None, stream=None):
+    import torch
+    _need(scores, torch.float32, "scores")
+    _need(row_len, torch.int32, "row_len")
+    _need(out_idx, torch.int32, "out_idx")
+    rows = row_len.shape[0]
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("indexer_topk", load_library().indexer_topk(
+        _ptr(scores), scores.shape[1], _ptr(row_len), rows, max_row_len, k, _ptr(out_idx),
+        _ptr(ws), nbytes, _stream(stream)))
+
+
+def indexer_score_topk(q, w, cache: KCache, rows: Rows, k: int, out_idx, ws, out_scores=None,
+                       q_scale=None, stream=None):
+    import torch
+    q_dtype, heads = _q_args(q, q_scale, w)
+    _need(out_idx, torch.int32, "out_idx")
+    _need(out_scores, torch.float32, "out_scores")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("indexer_score_topk", load_library().indexer_score_topk(
+        _ptr(q), q_dtype, _ptr(q_scale), _ptr(w), heads, cache, rows, k, _ptr(out_idx),
+        _ptr(out_scores), _ptr(ws), nbytes, _stream(stream)))
+
+
+def alloc_workspace(op: int, rows: int, max_row_len: int, k: int, device="cuda"):
+    """A 256-byte aligned uint8 workspace tensor of the size the op needs (or None)."""
+    import torch
+    n = workspace_bytes(op, rows, max_row_len, k)
+    if n == 0:
+        return None
+    t = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-t.data_ptr()) % 256
+    return t[off:off + n]

@@ -1,0 +1,51 @@
+// Internal launchers: host functions, one per kernel family, called by the C ABI
+// layer after it has validated every argument.  Each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct KCache {
+  uint8_t* base;
+  int dtype;       // 1 bf16, 2 fp8
+  int block_size;  // 32 or 64
+  int64_t num_blocks;
+};
+
+struct Rows {
+  const int32_t* block_table;
+  int max_blocks;
+  int num_seqs;
+  const int32_t* row_seq;
+  const int32_t* row_len;
+  int rows;
+  int max_row_len;
+};
+
+hipError_t launch_store(const uint16_t* x, int64_t n, const int32_t* pos, const int64_t* slots,
+                        const KCache& c, uint32_t flags, float eps, float rope_base, int rope_dim,
+                        float* dbg, hipStream_t s);
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t n_vec, uint8_t* codes, float* scales,
+                            hipStream_t s);
+
+// bf16 queries against bf16 or fp8 keys (one query row per workgroup chunk; heads on
+// the MFMA M dimension).  write_pad: also write -inf in [row_len, max_row_len).
+hipError_t launch_score_decode(const uint16_t* q, const float* w, const KCache& c, const Rows& r,
+                               float* scores, int64_t ld, bool write_pad, hipStream_t s);
+
+// fp8 queries against fp8 keys (query tokens x heads on the MFMA M dimension).
+hipError_t launch_score_prefill(const uint8_t* q, const float* q_scale, const float* w,
+                                const KCache& c, const Rows& r, float* scores, int64_t ld,
+                                bool write_pad, hipStream_t s);
+
+// top-k over fp32 score rows; ws of topk_ws_bytes(rows, max_row_len, k) bytes.
+size_t topk_ws_bytes(int rows, int max_row_len, int k);
+hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_len, int rows,
+                       int max_row_len, int k, int32_t* out_idx, float* out_scores, void* ws,
+                       hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,227 @@
+// Decode scoring: one bf16 query row (64 index heads x 128) against the paged
+// index-K cache (bf16 keys, or fp8 e4m3 keys with a per-token fp32 scale):
+//     score[p] = s_p * sum_h w_h * max(0, q_h . k_p)
+// (the lightning-indexer q.k score of ROCm/ATOM issue 1507, "Root cause found"; the
+// paged read through the block table is the analog of the pages'
+// deepgemm_fp8_paged_mqa_logits, "How it was isolated").
+//
+// Design for gfx950:
+//  - All 64 heads of a row share every key (multi-query), so each 16-key group is a
+//    dense [64 x 128] . [128 x 16] product: four 16-head M tiles x four K=32 steps of
+//    v_mfma_f32_16x16x32_bf16.  At ~8 TB/s of fp8 keys the contraction needs
+//    ~0.5 P MAC/s, far beyond the vector ALU, so it must run on the matrix cores.
+//  - Each wavefront holds the whole query row as MFMA A operands in registers
+//    (64 VGPRs) and streams its own keys straight from HBM into B-operand registers:
+//    no LDS, no cross-wave reduction.  The contraction index d is permuted so that
+//    lane l reads one contiguous 64-byte (bf16) or 32-byte (fp8) run of key
+//    l mod 16 with 16-byte loads; A uses the same permutation, so the dot products
+//    are unchanged.
+//  - fp8 codes are widened to bf16 exactly (every e4m3 value is a bf16 value) with
+//    v_cvt_scalef32_pk_bf16_fp8; the per-key scale multiplies the head sum.
+//  - The ReLU-weighted head sum is in-lane (16 of the 64 heads per lane) plus two
+//    cross-lane adds; lane l ends up with the score of key 16*(l/16) + l%16 of a
+//    64-key span, so each span is stored with one coalesced 256-byte write.
+//  - Software pipeline: the next span's keys are loaded before the current span is
+//    computed.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int kSpan = 64;  // keys per span (one 64-token block, or two 32-token blocks)
+
+template <bool kFp8>
+struct SpanRaw;
+template <>
+struct SpanRaw<true> {
+  uint4 c[4][2];  // per 16-key group: 32 code bytes of this lane's key
+  float s[4];     // per group: scale of this lane's key
+};
+template <>
+struct SpanRaw<false> {
+  uint4 c[4][4];  // per 16-key group: 64 bytes (32 bf16) of this lane's key
+};
+
+// Loads the keys of one 64-key span for this lane.  Groups at or past the row's
+// length are not touched (their block-table entries may not exist); a block id
+// outside the pool marks the span bad and reads block 0 instead.
+template <bool kFp8, int BS>
+__device__ __forceinline__ void load_span(SpanRaw<kFp8>& raw, bool& bad, const uint8_t* cache,
+                                          int64_t num_blocks, const int32_t* bt_row, int p_span,
+                                          int n, int lane) {
+  bad = false;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int p0 = p_span + 16 * g;
+    if (p0 >= n) continue;  // uniform per wave
+    int phys = bt_row[p0 / BS];
+    if (phys < 0 || phys >= num_blocks) {
+      bad = true;
+      phys = 0;
+    }
+    const int off = (p0 % BS) + (lane & 15);
+    if constexpr (kFp8) {
+      const uint8_t* blk = cache + (int64_t)phys * (BS * 132);
+      const uint4* src = reinterpret_cast<const uint4*>(blk + off * 128 + 32 * (lane >> 4));
+      raw.c[g][0] = src[0];
+      raw.c[g][1] = src[1];
+      raw.s[g] = reinterpret_cast<const float*>(blk + BS * 128)[off];
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(cache + ((int64_t)phys * BS + off) * 256 +
+                                                        64 * (lane >> 4));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) raw.c[g][s] = src[s];
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  union {
+    bf16x2_t h[4];
+    bf16x8_t v;
+  } u;
+  u.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
+  u.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
+  u.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false);
+  u.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
+  return u.v;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  union {
+    uint4 u;
+    bf16x8_t b;
+  } x;
+  x.u = v;
+  return x.b;
+}
+
+template <bool kFp8, int BS>
+__global__ __launch_bounds__(256, 2) void score_decode_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
+    int64_t num_blocks, const int32_t* __restrict__ block_table, int max_blocks, int num_seqs,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_len, int max_row_len,
+    float* __restrict__ scores, int64_t ld, int spans_per_wave, int write_pad) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = blockIdx.y;
+  const int seq = row_seq[r];
+  const int n = min(max(row_len[r], 0), max_row_len);
+  float* out = scores + (int64_t)r * ld;
+  const int chunk0 = blockIdx.x * (4 * spans_per_wave * kSpan);
+  const bool seq_bad = seq < 0 || seq >= num_seqs;
+
+  if (chunk0 >= n || seq_bad) {  // nothing to read: padding, or NaN for a bad sequence
+    const int end = min(chunk0 + 4 * spans_per_wave * kSpan, max_row_len);
+    for (int p = chunk0 + (int)threadIdx.x; p < end; p += 256) {
+      if (p < n) out[p] = __builtin_nanf("");
+      else if (write_pad) out[p] = -INFINITY;
+    }
+    return;
+  }
+
+  // A operands: head 16*mt + lane%16, dims 32*(lane/16) + 8*s .. +7
+  bf16x8_t qa[4][4];
+  {
+    const uint16_t* qr = q + (int64_t)r * 64 * kHeadDim;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            qr + (16 * mt + (lane & 15)) * kHeadDim + 32 * (lane >> 4) + 8 * s));
+  }
+  // weights of the accumulator rows this lane holds: head 16*mt + 4*(lane/16) + v
+  float wv[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wv[mt][v] = w[(int64_t)r * 64 + 16 * mt + 4 * (lane >> 4) + v];
+
+  const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
+
+  SpanRaw<kFp8> cur, nxt;
+  bool cur_bad = false, nxt_bad = false;
+  int p_span = chunk0 + wave * kSpan;
+  if (p_span < n) load_span<kFp8, BS>(cur, cur_bad, cache, num_blocks, bt_row, p_span, n, lane);
+
+  for (int i = 0; i < spans_per_wave; ++i, p_span += 4 * kSpan) {
+    const int p_next = p_span + 4 * kSpan;
+    if (i + 1 < spans_per_wave && p_next < n)
+      load_span<kFp8, BS>(nxt, nxt_bad, cache, num_blocks, bt_row, p_next, n, lane);
+
+    if (p_span < n) {
+      float val = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8_t b;
+          if constexpr (kFp8) {
+            const uint4 c = cur.c[g][s >> 1];
+            b = (s & 1) ? fp8x8_to_bf16x8(c.z, c.w) : fp8x8_to_bf16x8(c.x, c.y);
+          } else {
+            b = as_bf16x8(cur.c[g][s]);
+          }
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], b, acc[mt], 0, 0, 0);
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) part = fmaf(wv[mt][v], fmaxf(acc[mt][v], 0.0f), part);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if constexpr (kFp8) part *= cur.s[g];
+        if ((lane >> 4) == g) val = part + 0.0f;  // +0.0f: a zero score is +0
+      }
+      const int p = p_span + lane;
+      if (p >= n) val = -INFINITY;
+      if (cur_bad) val = __builtin_nanf("");
+      if (p < max_row_len) out[p] = val;
+    } else if (write_pad) {
+      const int p = p_span + lane;
+      if (p < max_row_len) out[p] = -INFINITY;
+    }
+    cur = nxt;
+    cur_bad = nxt_bad;
+  }
+}
+
+template <bool kFp8>
+hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const Rows& r,
+                     float* scores, int64_t ld, bool write_pad, hipStream_t s) {
+  const int64_t spans_row = (r.max_row_len + kSpan - 1) / kSpan;
+  const int64_t total = spans_row * r.rows;
+  // aim for >= ~4 workgroups per CU on the 256-CU part, at most 8 spans per wave
+  int spw = (int)(total / (4 * 1024));
+  spw = spw < 1 ? 1 : (spw > 8 ? 8 : spw);
+  const int64_t per_wg = 4LL * spw;
+  const dim3 grid((unsigned)((spans_row + per_wg - 1) / per_wg), (unsigned)r.rows), block(256);
+  if (c.block_size == 64)
+    hipLaunchKernelGGL((score_decode_kernel<kFp8, 64>), grid, block, 0, s, q, w, c.base,
+                       c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
+                       r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
+  else
+    hipLaunchKernelGGL((score_decode_kernel<kFp8, 32>), grid, block, 0, s, q, w, c.base,
+                       c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
+                       r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_decode(const uint16_t* q, const float* w, const KCache& c, const Rows& r,
+                               float* scores, int64_t ld, bool write_pad, hipStream_t s) {
+  if (r.rows == 0 || r.max_row_len == 0) return hipSuccess;
+  return c.dtype == 2 ? launch_bs<true>(q, w, c, r, scores, ld, write_pad, s)
+                      : launch_bs<false>(q, w, c, r, scores, ld, write_pad, s);
+}
+
+}  // namespace dsa

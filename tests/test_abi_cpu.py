@@ -1,0 +1,143 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every entry point
+include/dsa_indexer.h declares, and rejects bad arguments on the host before any
+launch (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_token_store_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = dsa.load_library()
+    names = declared_functions()
+    assert set(names) == set(dsa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.indexer_abi_version() == 1
+
+
+FAKE = 1 << 20          # never dereferenced: every call below fails validation first
+ALIGNED = 1 << 24
+
+
+def cache(dtype=dsa.IDX_FP8_E4M3, bs=64, nb=10, base=ALIGNED):
+    return dsa.KCache(base, dtype, bs, nb)
+
+
+def rows(n=4, max_row_len=100, max_blocks=4, num_seqs=2):
+    return dsa.Rows(FAKE, max_blocks, num_seqs, FAKE, FAKE, n, max_row_len)
+
+
+def err(lib):
+    return lib.indexer_last_error().decode()
+
+
+def test_store_validation():
+    lib = dsa.load_library()
+    f = lib.index_k_store
+    assert f(FAKE, -1, None, FAKE, cache(), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 4, None, FAKE, cache(), 8, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert "flag" in err(lib)
+    assert f(FAKE, 4, None, FAKE, cache(base=ALIGNED + 16), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert "aligned" in err(lib)
+    assert f(FAKE, 4, None, FAKE, cache(bs=16), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EUNSUPPORTED
+    assert f(FAKE, 4, None, FAKE, cache(dtype=3), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 4, FAKE, FAKE, cache(), dsa.IDX_STORE_ROPE, 1e-6, 1e4, 63, None, None) == dsa.IDX_EINVAL
+    assert "rope_dim" in err(lib)
+    assert f(FAKE, 4, FAKE, FAKE, cache(), dsa.IDX_STORE_ROPE, 1e-6, -1.0, 64, None, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 4, None, FAKE, cache(), dsa.IDX_STORE_ROPE, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert "positions" in err(lib)
+    assert f(FAKE, 4, None, FAKE, cache(), dsa.IDX_STORE_RMSNORM, -1.0, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert f(None, 4, None, FAKE, cache(), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert f(FAKE + 2, 4, None, FAKE, cache(), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 4, None, FAKE + 4, cache(), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    # n = 0 is a no-op that never touches the GPU
+    assert f(None, 0, None, None, cache(), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_OK
+    assert err(lib) == ""
+
+
+def test_quant_validation():
+    lib = dsa.load_library()
+    f = lib.indexer_quant_fp8
+    assert f(FAKE, -3, FAKE, FAKE, None) == dsa.IDX_EINVAL
+    assert f(None, 3, FAKE, FAKE, None) == dsa.IDX_EINVAL
+    assert f(FAKE + 8, 3, FAKE, FAKE, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 3, FAKE + 4, FAKE, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 0, None, None, None) == dsa.IDX_OK
+
+
+def test_score_validation():
+    lib = dsa.load_library()
+    f = lib.indexer_score
+    ok = dict(q=FAKE, qd=dsa.IDX_BF16, qs=None, w=FAKE, h=64, c=cache(), r=rows(), s=FAKE, ld=128)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["q"], a["qd"], a["qs"], a["w"], a["h"], a["c"], a["r"], a["s"], a["ld"], None)
+
+    assert call(h=32) == dsa.IDX_EUNSUPPORTED and "heads" in err(lib)
+    assert call(qd=dsa.IDX_FP8_E4M3, c=cache(dtype=dsa.IDX_BF16), qs=FAKE) == dsa.IDX_EUNSUPPORTED
+    assert call(qd=dsa.IDX_FP8_E4M3) == dsa.IDX_EINVAL and "q_scale" in err(lib)
+    assert call(qd=7) == dsa.IDX_EINVAL
+    assert call(ld=99) == dsa.IDX_EINVAL and "ld" in err(lib)
+    assert call(r=rows(max_row_len=300)) == dsa.IDX_EINVAL          # > max_blocks * block_size
+    assert call(r=rows(n=70000)) == dsa.IDX_EINVAL
+    assert call(r=rows(n=-1)) == dsa.IDX_EINVAL
+    assert call(q=FAKE + 8) == dsa.IDX_EINVAL
+    assert call(s=None) == dsa.IDX_EINVAL
+    assert call(c=cache(nb=0)) == dsa.IDX_EINVAL
+    assert call(r=dsa.Rows(None, 4, 2, FAKE, FAKE, 4, 100)) == dsa.IDX_EINVAL
+    assert call(r=rows(n=0)) == dsa.IDX_OK
+
+
+def test_topk_validation_and_workspace():
+    lib = dsa.load_library()
+    f = lib.indexer_topk
+    assert f(FAKE, 100, FAKE, 4, 100, 0, FAKE, None, 0, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 100, FAKE, 4, 100, 8193, FAKE, None, 0, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 99, FAKE, 4, 100, 8, FAKE, None, 0, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 100, None, 4, 100, 8, FAKE, None, 0, None) == dsa.IDX_EINVAL
+    # long rows need a workspace; too small is refused before any launch
+    need = lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, 4, 1 << 20, 1024)
+    assert need > 0
+    assert lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, 4, 20000, 512) == 0
+    assert f(FAKE, 1 << 20, FAKE, 4, 1 << 20, 1024, FAKE, ALIGNED, need - 1, None) == dsa.IDX_EWORKSPACE
+    assert f(FAKE, 1 << 20, FAKE, 4, 1 << 20, 1024, FAKE, ALIGNED + 64, need, None) == dsa.IDX_EINVAL
+    st = lib.indexer_score_topk
+    need2 = lib.indexer_workspace_bytes(dsa.IDX_OP_SCORE_TOPK, 4, 100, 8)
+    assert need2 >= 4 * 128 * 4
+    assert st(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 8, FAKE, None, ALIGNED, need2 - 1, None) == dsa.IDX_EWORKSPACE
+    assert st(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 0, FAKE, None, ALIGNED, need2, None) == dsa.IDX_EINVAL
+    assert lib.indexer_workspace_bytes(99, 4, 100, 8) == 0
+    assert lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, 4, 100, 0) == 0
+
+
+def test_error_string_is_thread_local():
+    import threading
+    lib = dsa.load_library()
+    out = {}
+
+    def worker():
+        lib.indexer_quant_fp8(FAKE, -1, FAKE, FAKE, None)
+        out["t"] = err(lib)
+
+    lib.indexer_quant_fp8(FAKE, 0, None, None, None)   # success clears this thread's error
+    t = threading.Thread(target=worker)
+    t.start()
+    t.join()
+    assert "n_vec" in out["t"]
+    assert err(lib) == ""

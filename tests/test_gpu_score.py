@@ -1,0 +1,110 @@
+"""HIP indexer_score against the oracle (C1), page-table invariance, determinism."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_token_store_amd as dsa
+from oracle import oracle as O
+from synth import gen
+
+from _hip import GpuWorkload, i32, note
+from _parity import RTOL, OracleKeys, check_scores, oracle_scores
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_scores(g: GpuWorkload, ld=None, fp8_q=False):
+    wl = g.wl
+    ld = ld or wl.max_row_len + 7
+    out = torch.full((wl.rows, ld), 12345.0, dtype=torch.float32, device="cuda")
+    q, qs = g.query(fp8_q)
+    note(f"indexer_score {wl.name} {g.key_dtype} rows={wl.rows} max_len={wl.max_row_len} bs={wl.block_size}")
+    dsa.indexer_score(q, g.w, g.cache, g.rows, out, q_scale=qs)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, wl.max_row_len:] == 12345.0), "columns beyond max_row_len must not be written"
+    return o
+
+
+CASES = [
+    # config, scale, key dtype, block size
+    (1, 1.0, "bf16", 64),
+    (1, 1.0, "fp8", 32),
+    (2, 0.1, "fp8", 64),
+    (2, 0.1, "bf16", 32),
+    (3, 0.02, "bf16", 64),
+    (3, 0.02, "fp8", 64),
+    (5, 0.004, "fp8", 64),
+]
+
+
+@pytest.mark.parametrize("cfg,scale,kd,bs", CASES)
+def test_score_matches_oracle(cfg, scale, kd, bs):
+    wl = gen.config(cfg, scale=scale, block_size=bs, key_dtype=kd if cfg != 4 else None)
+    g = GpuWorkload(wl, key_dtype=kd)
+    g.store_new()
+    got = gpu_scores(g)
+    ok = OracleKeys(wl, kd)
+    o = oracle_scores(wl, ok)
+    stats = check_scores(got, o, wl.row_len, RTOL[kd], slack=ok.slack())
+    print(stats)
+
+
+def test_page_table_permutation_is_bit_invariant():
+    # identical logical keys behind the identity table and behind a shuffled one
+    wl_id = gen.config(2, scale=0.05, shuffle=False)
+    wl_sh = gen.config(2, scale=0.05, shuffle=True)
+    assert not np.array_equal(wl_id.block_table, wl_sh.block_table)
+    a = gpu_scores(GpuWorkload(wl_id))
+    b = gpu_scores(GpuWorkload(wl_sh))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_deterministic_and_ld_independent():
+    wl = gen.config(2, scale=0.05)
+    g = GpuWorkload(wl)
+    a = gpu_scores(g)
+    b = gpu_scores(g, ld=wl.max_row_len + 300)
+    assert np.array_equal(a[:, :wl.max_row_len].view(np.uint32), b[:, :wl.max_row_len].view(np.uint32))
+
+
+def test_ragged_rows_and_edge_lengths():
+    # rows of length 0, 1, 15, 16, 17, 63, 64, 65 and one spanning many blocks
+    lens = np.array([0, 1, 15, 16, 17, 63, 64, 65, 777], np.int64)
+    wl = gen.make(np.maximum(lens, 1), key_dtype="fp8", k=4, needle_depth=None, seed=5)
+    wl.row_len = lens.astype(np.int32)
+    g = GpuWorkload(wl)
+    got = gpu_scores(g)
+    o = oracle_scores(wl, OracleKeys(wl))
+    check_scores(got, o, wl.row_len, RTOL["fp8"])
+
+
+def test_rows_sharing_a_sequence():
+    # several query rows reading one sequence with different causal lengths
+    wl = gen.make([3000], key_dtype="bf16", k=64, needle_depth=None, prefill_rows=40, seed=6)
+    g = GpuWorkload(wl, key_dtype="bf16")
+    got = gpu_scores(g)
+    check_scores(got, oracle_scores(wl, OracleKeys(wl, "bf16")), wl.row_len, RTOL["bf16"])
+
+
+def test_bad_block_id_scores_nan_without_faulting():
+    # a block id outside the pool is caught by the kernel's bounds check: the
+    # affected 16-key groups score NaN, nothing is read out of bounds
+    wl = gen.config(1, scale=0.2)
+    bt = wl.block_table.copy()
+    bt[0, 1] = wl.num_blocks + 5
+    g = GpuWorkload(wl, block_table=bt)
+    got = gpu_scores(g)
+    n = int(wl.row_len[0])
+    bs = wl.block_size
+    assert np.all(np.isnan(got[0, bs:min(2 * bs, n)]))
+    assert np.all(np.isfinite(got[0, :bs]))
+
+
+def test_needle_ranks_first_on_gpu_scores():
+    for S in (2000, 4500, 10000, 22000):
+        for kd in ("bf16", "fp8"):
+            wl = gen.make([S], key_dtype=kd, k=512, seed=0, shuffle=True)
+            got = gpu_scores(GpuWorkload(wl, key_dtype=kd))
+            p = int(wl.needle_pos[0])
+            assert O.rank_of(got[0].astype(np.float64), S, p) == 1

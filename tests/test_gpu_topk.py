@@ -1,0 +1,87 @@
+"""HIP indexer_topk against the oracle's sort-based top-k, bit-exact (C3), on
+synthetic score rows: ties, signed zeros, ragged causal lengths, and rows long
+enough to need several reduction levels."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_token_store_amd as dsa
+from oracle import oracle as O
+from synth import gen
+
+from _hip import f32, i32, note
+
+pytestmark = pytest.mark.gpu
+
+
+def run_topk(scores: np.ndarray, row_len: np.ndarray, max_row_len: int, k: int, ld=None):
+    rows = scores.shape[0]
+    ld = ld or scores.shape[1]
+    s = torch.full((rows, ld), float("nan"), dtype=torch.float32, device="cuda")
+    s[:, :scores.shape[1]] = f32(scores)
+    out = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    ws = dsa.alloc_workspace(dsa.IDX_OP_TOPK, rows, max_row_len, k)
+    note(f"indexer_topk rows={rows} max_len={max_row_len} k={k} ws={0 if ws is None else ws.numel()}")
+    dsa.indexer_topk(s, i32(row_len), max_row_len, k, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+CASES = [
+    # rows, n, k, kind
+    (4, 2000, 512, "normal"),
+    (4, 2000, 512, "ties"),
+    (3, 2000, 512, "equal"),
+    (3, 3000, 100, "increasing"),
+    (3, 3000, 100, "decreasing"),
+    (4, 5000, 700, "signed_zero"),
+    (4, 22000, 512, "heavy"),
+    (8, 22000, 512, "ties"),
+    (4, 36864, 1024, "heavy"),
+    (2, 36864, 1024, "ties"),
+    (2, 131072, 1024, "normal"),
+    (2, 131072, 1024, "ties"),
+    (1, 200000, 2048, "heavy"),
+    (2, 100000, 8192, "normal"),
+    (3, 1000, 1, "normal"),
+    (3, 1000, 7, "ties"),
+]
+
+
+@pytest.mark.parametrize("rows,n,k,kind", CASES)
+def test_topk_bit_exact(rows, n, k, kind):
+    x = gen.score_rows_for_topk(rows, n, kind=kind, seed=rows * 7 + k)
+    rng = np.random.default_rng(n + k)
+    lens = np.full(rows, n, np.int64)
+    if rows > 1:
+        lens[1:] = rng.integers(1, n + 1, size=rows - 1)
+    got = run_topk(x, lens, n, k)
+    want = O.topk(x, lens, k)
+    for r in range(rows):
+        assert np.array_equal(got[r], want[r]), (r, int(lens[r]), np.setdiff1d(got[r], want[r])[:5],
+                                                 np.setdiff1d(want[r], got[r])[:5])
+
+
+def test_topk_edge_lengths():
+    k = 512
+    lens = np.array([0, 1, k - 1, k, k + 1, 1023, 1024, 1025, 4096, 4097, 32768], np.int64)
+    n = int(lens.max())
+    x = gen.score_rows_for_topk(len(lens), n, kind="ties", seed=3)
+    got = run_topk(x, lens, n, k, ld=n + 5)
+    assert np.array_equal(got, O.topk(x, lens, k))
+
+
+def test_topk_long_rows_1m():
+    n, k = 1 << 20, 1024
+    x = gen.score_rows_for_topk(2, n, kind="heavy", seed=9)
+    lens = np.array([n, n - 12345], np.int64)
+    got = run_topk(x, lens, n, k)
+    assert np.array_equal(got, O.topk(x, lens, k))
+
+
+def test_topk_deterministic():
+    x = gen.score_rows_for_topk(8, 40000, kind="ties", seed=1)
+    lens = np.full(8, 40000)
+    a = run_topk(x, lens, 40000, 1024)
+    b = run_topk(x, lens, 40000, 1024)
+    assert np.array_equal(a, b)
