@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA indexer hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input, with every
+input already resident in HBM:
+  decode workloads   index_k_store of the step's new tokens (RMSNorm -> RoPE ->
+                     Hadamard -> fp8 -> paged scatter), indexer_score over the
+                     paged cache, indexer_topk of every row
+  prefill workload   indexer_quant_fp8 of the queries, indexer_score (fp8 x fp8),
+                     indexer_topk
+These are exactly the kernels indexer_score_topk chains; calling the three entry
+points separately lets HIP events on the launch stream time each kernel inside the
+timed region.  Key caches are replicated and rotated so that every step reads its
+keys from HBM, not from the 256 MB last-level cache.
+
+Prints one JSON line.  Metric: visible (query, key) pairs scored per second for the
+whole step, with top-k selections per second beside it; `roofline` reports the
+dominant kernel against the HBM (decode) or fp8 MFMA (prefill) peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer keys scored/s + top-k selections/s at 1 GPU; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
+COLD_BYTES = 640 << 20          # replicas of the key cache cover at least this much
+
+WORKLOADS = {
+    # name: (config, key dtype, description)
+    "decode_b32": (2, "fp8", "decode batch 32, S~U[4500,22000], fp8 keys, top-512"),
+    "tiny_decode": (1, "bf16", "decode 1 x 2000, bf16 keys, top-512"),
+    "ab_bf16": (3, "bf16", "decode 16 x 131072, bf16 keys, top-1024"),
+    "ab_fp8": (3, "fp8", "decode 16 x 131072, fp8 keys, top-1024"),
+    "prefill": (4, "fp8", "chunked prefill 4096 rows on a 32768 prefix, fp8 keys, top-1024"),
+    "long_decode": (5, "fp8", "decode 4 x 1048576 fp8 keys after a 4096-token store, top-1024"),
+}
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparse_attention_token_store_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"score_decode": ["score_decode.hip", "common.hpp"],
+                  "score_prefill": ["score_prefill.hip", "common.hpp"]}
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if the summary in
+    profiles/ was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    h = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m.group(1))
+
+
+class Runner:
+    def __init__(self, name: str, replicas: int | None):
+        import torch
+        import sparse_attention_token_store_amd as dsa
+        from synth import gen
+        self.torch, self.dsa, self.name = torch, dsa, name
+        cfg, kd, self.desc = WORKLOADS[name]
+        wl = gen.config(cfg, key_dtype=kd)
+        self.wl, self.kd = wl, kd
+        dev = "cuda"
+        self.dtype = dsa.IDX_BF16 if kd == "bf16" else dsa.IDX_FP8_E4M3
+        cbytes = dsa.cache_bytes(self.dtype, wl.block_size, wl.num_blocks)
+        self.replicas = replicas or max(1, -(-COLD_BYTES // cbytes))
+
+        def t_bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def t(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+
+        x, slots = wl.prefix_tokens()
+        x_t, slots_t = t_bf16(x), t(slots, np.int64)
+        self.bufs, self.caches = [], []
+        for _ in range(self.replicas):
+            b = torch.empty(cbytes, dtype=torch.uint8, device=dev)
+            c = dsa.kcache(b, self.dtype, wl.block_size, wl.num_blocks)
+            dsa.index_k_store(x_t, None, slots_t, c, 0)
+            self.bufs.append(b)
+            self.caches.append(c)
+        del x_t, slots_t
+        self.block_table = t(wl.block_table, np.int32)
+        self.row_seq, self.row_len = t(wl.row_seq, np.int32), t(wl.row_len, np.int32)
+        self.rows = dsa.rows_desc(self.block_table, self.row_seq, self.row_len, wl.max_row_len)
+        self.q = t_bf16(wl.q_bits)
+        self.w = t(wl.w, np.float32)
+        self.new_x, self.new_pos = t_bf16(wl.new_x_bits), t(wl.new_pos, np.int32)
+        self.new_slots = t(wl.new_slots(), np.int64)
+        self.prefill = wl.q_dtype == "fp8"
+        if self.prefill:
+            self.q_codes = torch.empty(self.q.shape, dtype=torch.uint8, device=dev)
+            self.q_scale = torch.empty(self.q.shape[:2], dtype=torch.float32, device=dev)
+        self.ld = -(-wl.max_row_len // 64) * 64
+        self.scores = torch.empty((wl.rows, self.ld), dtype=torch.float32, device=dev)
+        self.out_idx = torch.empty((wl.rows, wl.k), dtype=torch.int32, device=dev)
+        self.ws = dsa.alloc_workspace(dsa.IDX_OP_TOPK, wl.rows, wl.max_row_len, wl.k)
+        torch.cuda.synchronize()
+
+    def step(self, i, ev=None):
+        """One pass of the hot path on replica i % R.  ev: optional list of 4 events
+        recorded around the score kernel and the top-k."""
+        dsa, wl = self.dsa, self.wl
+        cache = self.caches[i % self.replicas]
+        if wl.new_x_bits.shape[0]:
+            dsa.index_k_store(self.new_x, self.new_pos, self.new_slots, cache, dsa.IDX_STORE_ALL,
+                              wl.rms_eps, wl.rope_base, wl.rope_dim)
+        if self.prefill:
+            dsa.indexer_quant_fp8(self.q, self.q_codes, self.q_scale)
+        if ev:
+            ev[0].record()
+        if self.prefill:
+            dsa.indexer_score(self.q_codes, self.w, cache, self.rows, self.scores, q_scale=self.q_scale)
+        else:
+            dsa.indexer_score(self.q, self.w, cache, self.rows, self.scores)
+        if ev:
+            ev[1].record()
+        dsa.indexer_topk(self.scores, self.row_len, wl.max_row_len, wl.k, self.out_idx, self.ws)
+        if ev:
+            ev[2].record()
+
+    # algorithmic work of the dominant (score) kernel per launch
+    def score_work(self):
+        wl = self.wl
+        keys = wl.visible_keys
+        if self.prefill:
+            flops = 2.0 * wl.heads * 128 * keys
+            return {"bound": "mfma", "unit": "TFLOP/s", "work": flops, "peak": FP8_MFMA_PEAK_TFLOPS,
+                    "kernel": "score_prefill"}
+        key_bytes = 132 if self.kd == "fp8" else 256
+        per_key = key_bytes + 4 + 4.0 / wl.block_size          # key, score write, table entry
+        per_row = wl.heads * 128 * 2 + wl.heads * 4 + 8         # q (bf16), w, row_seq + row_len
+        pad = sum(wl.max_row_len - int(n) for n in wl.row_len) * 4   # -inf padding writes
+        nbytes = keys * per_key + wl.rows * per_row + pad
+        return {"bound": "hbm", "unit": "GB/s", "work": nbytes, "peak": HBM_PEAK_GBS,
+                "kernel": "score_decode"}
+
+
+def cpu_baseline(wl, kd, budget_s=15.0):
+    """The oracle (numpy float64, BLAS threads as configured) on a bounded sample of
+    the same workload: whole rows (store chain of the row's new tokens, key
+    dequantisation, score, top-k), as many as fit the time budget."""
+    from oracle import oracle as O
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = None
+    rows_done, keys_done, t_total = 0, 0, 0.0
+    order = np.argsort(wl.row_len)[::-1] if wl.rows > 1 else np.arange(wl.rows)
+    prefix_cache = {}
+    for r in order:
+        b = int(wl.row_seq[r])
+        n = int(wl.row_len[r])
+        if b not in prefix_cache:               # cache fill: not timed (setup)
+            x = wl.keys_bits[b]
+            if kd == "fp8":
+                prefix_cache[b] = O.quant_fp8(O.bf16_bits_to_f32(x))
+            else:
+                prefix_cache[b] = x
+        t0 = time.perf_counter()
+        sel = wl.new_seq == b
+        parts = []
+        store = prefix_cache[b]
+        nstored = int(wl.stored_len[b])
+        for p0 in range(0, min(n, nstored), 1 << 16):
+            p1 = min(n, nstored, p0 + (1 << 16))
+            parts.append(O.dequant_fp8(store[0][p0:p1], store[1][p0:p1]) if kd == "fp8"
+                         else O.bf16_bits_to_f64(store[p0:p1]))
+        if n > nstored:
+            y = O.store_chain(wl.new_x_bits[sel], wl.new_pos[sel], 7, wl.rms_eps, wl.rope_base, wl.rope_dim)
+            parts.append(O.dequant_fp8(*O.quant_fp8(y.astype(np.float32))) if kd == "fp8" else y)
+        keys = np.concatenate(parts, 0)[:n]
+        q = O.bf16_bits_to_f64(wl.q_bits[r])
+        if wl.q_dtype == "fp8":
+            c, s = O.quant_fp8(O.bf16_bits_to_f32(wl.q_bits[r]))
+            q = O.dequant_fp8(c, s)
+        sc = O.score(q, wl.w[r].astype(np.float64), keys)
+        O.topk(sc[None], [n], wl.k)
+        t_total += time.perf_counter() - t0
+        rows_done += 1
+        keys_done += n
+        if t_total >= budget_s:
+            break
+    return {"value": keys_done / t_total, "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} of {wl.rows} rows ({keys_done} visible keys) of the same workload, "
+                      f"{t_total:.1f} s: store chain of the row's new tokens, fp8/bf16 key decode, "
+                      f"float64 score, sort-based top-k",
+            "selections_per_s": rows_done / t_total}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_b32", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=None, help="key-cache replicas (default: cold-cache rotation)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a device copy of this many MiB (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+    if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
+        print("single-GPU benchmark: run without torch.distributed", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    run = Runner(args.workload, args.replicas)
+    wl = run.wl
+    print(f"[bench] {args.workload}: {run.desc}; rows={wl.rows} visible_keys={wl.visible_keys} "
+          f"replicas={run.replicas}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        run.step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        run.step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / args.steps
+    score_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    topk_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    keys = wl.visible_keys
+    value = keys / (ms / 1e3)
+    work = run.score_work()
+    achieved = work["work"] / (score_ms / 1e3) / (1e9 if work["unit"] == "GB/s" else 1e12)
+    traffic = traffic_from_profile(work["kernel"], args.workload)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not run.prefill else "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "description": run.desc,
+            "rows": wl.rows,
+            "visible_keys": keys,
+            "max_row_len": wl.max_row_len,
+            "k": wl.k,
+            "heads": wl.heads,
+            "head_dim": 128,
+            "key_dtype": run.kd,
+            "q_dtype": wl.q_dtype,
+            "block_size": wl.block_size,
+            "new_tokens_stored_per_step": int(wl.new_x_bits.shape[0]),
+            "cache_replicas": run.replicas,
+            "parallelism": "single GPU",
+        },
+        "selections_per_s": wl.rows / (ms / 1e3),
+        "kernel_ms": {"score": score_ms, "topk": topk_ms},
+        "roofline": {
+            "bound": work["bound"],
+            "kernel": work["kernel"],
+            "achieved": achieved,
+            "peak": work["peak"],
+            "unit": work["unit"],
+            "frac": achieved / work["peak"],
+            "traffic": traffic,
+            "algorithmic_per_launch": work["work"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, run.kd, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

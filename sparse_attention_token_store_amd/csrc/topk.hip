@@ -3,14 +3,22 @@
 // padded with -1 (ROCm/ATOM issue 1507, "Summary": index_topk 512/1024; "How it was
 // isolated": the per-row top-k must agree exactly with torch.topk).
 //
-// Exact radix select on order-preserving 32-bit keys, one 1024-thread workgroup
-// per chunk of up to 32K elements, keys held in registers:
-//   pass 1 histograms bits 31..21 (2048 LDS bins), pass 2 bits 20..10, pass 3
-//   bits 9..0, each pass restricted to the keys that share the prefix found so far;
-//   the boundary bin is located with a block-wide suffix count.  The pass loop
-//   stops early when every key of the boundary bin is needed.
-//   Then every key above the threshold is kept plus the lowest-position keys equal
-//   to it, compacted in position order with wave ballots and two block scans.
+// Exact selection on order-preserving 32-bit keys, one 1024-thread workgroup per
+// chunk of up to 36,864 elements held in registers (cyclic layout: element
+// j*1024 + t lives in thread t, slot j):
+//  1. Lower bound.  With k <= 1024 the threads are split into >= k groups; every
+//     group owns a key >= its group maximum, so the smallest group maximum t_lo has
+//     at least k keys at or above it and the k-th largest key tau >= t_lo.  Keys
+//     below t_lo (typically 85-95% of a row) take no further part in the search.
+//  2. One histogram pass (LDS, <= 2048 bins) over the keys >= t_lo, on the 11 bits
+//     just below the common prefix of t_lo and the row maximum, where the
+//     candidates actually differ; a single wavefront scans the bins from the top to
+//     find the bin holding the k-th key.
+//  3. The keys of that bin are gathered into LDS and their low bits resolved with
+//     one or two more histogram passes over that short list (or, when a long run
+//     of ties fills the bin, with passes over the registers).
+//  4. Every key above tau is kept plus the lowest-position keys equal to it,
+//     compacted in position order with wave ballots and one scan.
 // Rows longer than one chunk are reduced level by level: each chunk keeps its own
 // top-k (exact: an element of the row's top-k under the order (score desc,
 // position asc) is also in its chunk's top-k), the survivors stay in position
@@ -23,38 +31,12 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kLevelChunk = 16384;    // R = 16 for the reducing levels of long rows
-constexpr int kMaxSingle = 32768;     // R = 32: the largest chunk held in registers
+constexpr int kLevel0Chunk = 16384;    // first reducing level of long rows (R = 16)
+constexpr int kLevelNChunk = 32768;    // later reducing levels (R = 32)
+constexpr int kMaxR = 36;
+constexpr int kMaxSingle = kMaxR * kThreads;   // 36,864: one chunk
 constexpr uint32_t kMinKey = 1u << 21;  // smallest key a real element may take
-
-// exclusive block scan of one int per thread; `tot` receives the block total
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    int t = threadIdx.x < kWaves ? wsum[threadIdx.x] : 0;
-    int u = t;
-#pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const int y = __shfl_up(u, o);
-      if ((int)threadIdx.x >= o) u += y;
-    }
-    if (threadIdx.x < kWaves) wsum[kWaves + threadIdx.x] = u - t;  // exclusive
-    if (threadIdx.x == kWaves - 1) wsum[2 * kWaves] = u;            // total
-  }
-  __syncthreads();
-  const int r = wsum[kWaves + wave] + x - v;
-  tot = wsum[2 * kWaves];
-  __syncthreads();  // wsum may be reused right after
-  return r;
-}
+constexpr int kCandMax = 4096;          // boundary-bin keys gathered into LDS
 
 // number of candidates a row keeps after one level with chunk size C
 __device__ __host__ __forceinline__ int64_t after_level(int64_t n, int64_t C, int k) {
@@ -72,6 +54,80 @@ struct LevelChunks {  // chunk size of every level, passed by value
   int64_t c[8];
 };
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m));
+  return v;
+}
+
+// Run by one wavefront: find the bin (of nbins = 64 * PER, or fewer when PER = 1)
+// that holds the rem-th largest counted key, scanning from the top bin down.
+// Lane l owns the PER contiguous bins [nbins - (l+1)*PER, nbins - l*PER), read with
+// independent vector loads.  Writes info = {bin, count above the bin, count in it}.
+template <int PER>
+__device__ __forceinline__ void find_bin_t(const int* hist, int nbins, int rem, int* info) {
+  const int lane = lane_id();
+  const int lo = nbins - (lane + 1) * PER;
+  const bool has = lo >= 0;
+  int h[PER];
+  if constexpr (PER >= 4) {
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const int4 v = has ? reinterpret_cast<const int4*>(hist + lo)[q] : make_int4(0, 0, 0, 0);
+      h[4 * q] = v.x;
+      h[4 * q + 1] = v.y;
+      h[4 * q + 2] = v.z;
+      h[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) h[q] = has ? hist[lo + q] : 0;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) cnt += h[q];
+  int x = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  const int excl = x - cnt;
+  if (has && excl < rem && x >= rem) {
+    int above = excl, bin = -1, hb = 0;
+#pragma unroll
+    for (int q = PER - 1; q >= 0; --q) {  // from this lane's top bin down
+      if (bin < 0) {
+        if (above + h[q] >= rem) {
+          bin = lo + q;
+          hb = h[q];
+        } else {
+          above += h[q];
+        }
+      }
+    }
+    info[0] = bin;
+    info[1] = above;
+    info[2] = hb;
+  }
+}
+
+__device__ __forceinline__ void find_bin(const int* hist, int nbins, int rem, int* info) {
+  switch (nbins >> 6) {
+    case 32: find_bin_t<32>(hist, nbins, rem, info); break;
+    case 16: find_bin_t<16>(hist, nbins, rem, info); break;
+    case 8: find_bin_t<8>(hist, nbins, rem, info); break;
+    case 4: find_bin_t<4>(hist, nbins, rem, info); break;
+    case 2: find_bin_t<2>(hist, nbins, rem, info); break;
+    default: find_bin_t<1>(hist, nbins, rem, info); break;
+  }
+}
+
 // kFirst: source is the score matrix; else a candidate list.  kLast: write the
 // final out_idx / out_scores; else the next candidate list.
 template <int R, bool kFirst, bool kLast>
@@ -80,11 +136,14 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     const int32_t* __restrict__ row_len, int max_row_len, int k, int nlevel, LevelChunks chunks,
     int32_t* __restrict__ out_idx, float* __restrict__ out_scores) {
   constexpr int C = R * kThreads;
-  __shared__ int hist[2048];
-  __shared__ int cnt_gt[R * kWaves];
-  __shared__ int cnt_eq[R * kWaves];
-  __shared__ int wsum[2 * kWaves + 1];
+  constexpr int E = R * kWaves;  // (slot, wave) entries of the compaction
+  __shared__ __attribute__((aligned(16))) int hist[2048];
+  __shared__ uint32_t cand[kCandMax];
+  __shared__ int cnt_gt[E];
+  __shared__ int cnt_eq[E];
+  __shared__ uint32_t red_max[kWaves], red_min[kWaves];
   __shared__ int info[3];
+  __shared__ int ncand;
 
   const int r = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -103,10 +162,9 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   }
   if (nc <= 0) return;
 
-  // Slots past the chunk's end hold the sentinel key 0.  Real keys are clamped to
-  // >= 2^21 (this only touches negative-NaN bit patterns), so the sentinel sits
-  // alone in histogram bin 0 of pass 1, which the search never reaches while more
-  // than k real keys exist, and it never equals or exceeds a threshold.
+  // Slots past the chunk's end hold the sentinel key 0; real keys are clamped to
+  // >= 2^21 (this only touches negative-NaN bit patterns) and the lower bound is
+  // never below 2^21, so the sentinel is never counted or selected.
   uint32_t key[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
@@ -147,86 +205,168 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     return;
   }
 
-  // ---- radix select of the k-th largest key
-  uint32_t prefix = 0u, pmask = 0u;
+  // ---- 1. row maximum and the group-maximum lower bound t_lo
+  uint32_t tmax = 0u;
+#pragma unroll
+  for (int j = 0; j < R; ++j) tmax = max(tmax, key[j]);
+  uint32_t gmax = tmax;
+  if (k <= kThreads) {
+    int g = 1;  // lanes per group: the largest power of two <= 64 leaving >= k groups
+    while (g < 64 && kThreads / (2 * g) >= k) g *= 2;
+    for (int m = 1; m < g; m <<= 1) gmax = max(gmax, (uint32_t)__shfl_xor((int)gmax, m));
+  }
+  {
+    const uint32_t wmax = wave_max_u32(tmax), wmin = wave_min_u32(gmax);
+    if (lane == 0) {
+      red_max[wave] = wmax;
+      red_min[wave] = wmin;
+    }
+  }
+  for (int b = tid; b < 2048; b += kThreads) hist[b] = 0;
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  uint32_t M = 0u, tlo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    M = max(M, red_max[w]);
+    tlo = min(tlo, red_min[w]);
+  }
+  if (k > kThreads) tlo = kMinKey;
+  tlo = max(tlo, kMinKey);
+
+  // ---- 2./3. radix search for tau among keys >= t_lo
+  uint32_t prefix, pmask;
   int rem = k;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    const uint32_t dmask = (uint32_t)nb - 1u;
-    for (int b = tid; b < nb; b += kThreads) hist[b] = 0;
-    __syncthreads();
+  if (tlo >= M) {  // every counted key equals the maximum
+    prefix = M;
+    pmask = 0xFFFFFFFFu;
+  } else {
+    const int hi = 31 - __clz(tlo ^ M);
+    const int s1 = hi >= 10 ? hi - 10 : 0;
+    const int nb1 = hi - s1 + 1;
+    const uint32_t dm1 = (1u << nb1) - 1u;
 #pragma unroll
     for (int j = 0; j < R; ++j)
-      if ((key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1);
+      if (key[j] >= tlo) atomicAdd(&hist[(key[j] >> s1) & dm1], 1);
     __syncthreads();
-    // bins in descending order; thread t owns bins nb-1-(t*per) .. nb-per-(t*per)
-    const int per = nb / kThreads;
-    int cnt = 0;
-    for (int q = 0; q < per; ++q) cnt += hist[nb - 1 - (tid * per + q)];
-    int tot;
-    const int above0 = block_excl_scan(cnt, wsum, tot);
-    if (above0 < rem && above0 + cnt >= rem) {
-      int above = above0;
-      for (int q = 0; q < per; ++q) {
-        const int b = nb - 1 - (tid * per + q);
-        const int h = hist[b];
-        if (above + h >= rem) {
-          info[0] = b;
-          info[1] = above;
-          info[2] = h;
-          break;
+    if (wave == 0) find_bin(hist, 1 << nb1, rem, info);
+    __syncthreads();
+    const int b1 = info[0], h1 = info[2];
+    rem -= info[1];
+    const uint32_t hmask = hi >= 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
+    prefix = (M & hmask) | ((uint32_t)b1 << s1);
+    pmask = hmask | (dm1 << s1);
+    if (h1 != rem && s1 > 0) {
+      const bool in_lds = h1 <= kCandMax;
+      if (in_lds) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const bool cnd = key[j] >= tlo && (key[j] & pmask) == prefix;
+          const uint64_t bm = __ballot(cnd);
+          if (bm) {
+            int at = 0;
+            if (lane == 0) at = atomicAdd(&ncand, __popcll(bm));
+            at = __shfl(at, 0);
+            if (cnd) cand[at + lanes_below(bm)] = key[j];
+          }
         }
-        above += h;
+      }
+      int s = s1;
+      while (s > 0) {  // uniform
+        const int ns = s >= 11 ? s - 11 : 0;
+        const int nb = s - ns;
+        const uint32_t dm = (1u << nb) - 1u;
+        for (int b = tid; b < (1 << nb); b += kThreads) hist[b] = 0;
+        __syncthreads();
+        if (in_lds) {
+          for (int q = tid; q < h1; q += kThreads) {
+            const uint32_t kv = cand[q];
+            if ((kv & pmask) == prefix) atomicAdd(&hist[(kv >> ns) & dm], 1);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < R; ++j)
+            if (key[j] >= tlo && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> ns) & dm], 1);
+        }
+        __syncthreads();
+        if (wave == 0) find_bin(hist, 1 << nb, rem, info);
+        __syncthreads();
+        const int b = info[0], hb = info[2];
+        rem -= info[1];
+        prefix |= (uint32_t)b << ns;
+        pmask |= dm << ns;
+        s = ns;
+        if (hb == rem) break;  // the whole bin is selected
       }
     }
-    __syncthreads();
-    const int b = info[0], above = info[1], hb = info[2];
-    rem -= above;
-    prefix |= (uint32_t)b << shift;
-    pmask |= dmask << shift;
-    __syncthreads();
-    if (hb == rem) break;  // the whole boundary bin is selected
   }
 
-  // ---- compaction in position order: keys > threshold, then the first `rem`
-  // keys equal to it
+  // ---- 4. compaction in position order: keys above the threshold, then the first
+  // `rem` keys equal to it (only keys >= t_lo take part)
 #pragma unroll
   for (int j = 0; j < R; ++j) {
+    const bool live = key[j] >= tlo;
     const uint32_t mk = key[j] & pmask;
-    const uint64_t bgt = __ballot(mk > prefix);
-    const uint64_t beq = __ballot(mk == prefix);
+    const uint64_t bgt = __ballot(live && mk > prefix);
+    const uint64_t beq = __ballot(live && mk == prefix);
     if (lane == 0) {
       cnt_gt[j * kWaves + wave] = __popcll(bgt);
       cnt_eq[j * kWaves + wave] = __popcll(beq);
     }
   }
   __syncthreads();
-  {
-    const bool mine = tid < R * kWaves;
-    const int ce = mine ? cnt_eq[tid] : 0;
-    const int cg = mine ? cnt_gt[tid] : 0;
-    int tot;
-    const int eqb = block_excl_scan(ce, wsum, tot);
-    const int take = cg + min(max(rem - eqb, 0), ce);
-    const int selb = block_excl_scan(take, wsum, tot);
-    if (mine) {
-      cnt_eq[tid] = eqb;
-      cnt_gt[tid] = selb;
+  if (wave == 0) {  // exclusive scans over the (slot, wave) entries, in position order
+    constexpr int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int se = 0;
+    for (int q = 0; q < per; ++q)
+      if (e0 + q < E) se += cnt_eq[e0 + q];
+    int xe = se;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(xe, o);
+      if (lane >= o) xe += y;
     }
+    int run_eq = xe - se, take_sum = 0;
+    for (int q = 0; q < per; ++q)
+      if (e0 + q < E) {
+        const int ce = cnt_eq[e0 + q];
+        take_sum += cnt_gt[e0 + q] + min(max(rem - run_eq, 0), ce);
+        run_eq += ce;
+      }
+    int xs = take_sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(xs, o);
+      if (lane >= o) xs += y;
+    }
+    int run_sel = xs - take_sum;
+    run_eq = xe - se;
+    for (int q = 0; q < per; ++q)
+      if (e0 + q < E) {
+        const int ce = cnt_eq[e0 + q], cg = cnt_gt[e0 + q];
+        const int t = cg + min(max(rem - run_eq, 0), ce);
+        cnt_eq[e0 + q] = run_eq;
+        cnt_gt[e0 + q] = run_sel;
+        run_eq += ce;
+        run_sel += t;
+      }
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int li = j * kThreads + tid;
+    const bool live = key[j] >= tlo;
     const uint32_t mk = key[j] & pmask;
-    const bool gt = mk > prefix;
-    const bool eq = mk == prefix;
-    const uint64_t beq = __ballot(eq);
-    const bool sel = gt || (eq && cnt_eq[j * kWaves + wave] + lanes_below(beq) < rem);
-    const uint64_t bsel = __ballot(sel);
-    if (sel) emit(cnt_gt[j * kWaves + wave] + lanes_below(bsel), li, key[j]);
+    const bool gt = live && mk > prefix;
+    const bool eq = live && mk == prefix;
+    const uint64_t bany = __ballot(gt || eq);
+    if (bany) {
+      const uint64_t beq = __ballot(eq);
+      const bool sel = gt || (eq && cnt_eq[j * kWaves + wave] + lanes_below(beq) < rem);
+      const uint64_t bsel = __ballot(sel);
+      if (sel) emit(cnt_gt[j * kWaves + wave] + lanes_below(bsel), li, key[j]);
+    }
   }
 }
 
@@ -246,6 +386,7 @@ hipError_t launch_level(int R, dim3 grid, hipStream_t s, const float* scores, in
     DSA_TOPK_CASE(16)
     DSA_TOPK_CASE(24)
     DSA_TOPK_CASE(32)
+    DSA_TOPK_CASE(36)
     default:
       return hipErrorInvalidValue;
   }
@@ -262,9 +403,9 @@ struct Plan {
 };
 
 int pick_r(int64_t n) {
-  for (int R : {4, 8, 16, 24, 32})
+  for (int R : {4, 8, 16, 24, 32, 36})
     if ((int64_t)R * kThreads >= n) return R;
-  return 32;
+  return kMaxR;
 }
 
 Plan make_plan(int max_row_len, int k) {
@@ -272,7 +413,7 @@ Plan make_plan(int max_row_len, int k) {
   int64_t n = max_row_len;
   p.len[0] = n;
   while (n > kMaxSingle) {
-    int64_t C = kLevelChunk;
+    int64_t C = p.levels == 0 ? kLevel0Chunk : kLevelNChunk;
     while (C < 2LL * k) C *= 2;  // each level must shrink the list (C <= 32768 for k <= 8192)
     p.chunk[p.levels] = C;
     n = after_level(n, C, k);

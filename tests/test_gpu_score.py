@@ -108,3 +108,49 @@ def test_needle_ranks_first_on_gpu_scores():
             got = gpu_scores(GpuWorkload(wl, key_dtype=kd))
             p = int(wl.needle_pos[0])
             assert O.rank_of(got[0].astype(np.float64), S, p) == 1
+
+
+def oracle_fp8_q(wl):
+    """The oracle's own fp8 queries: the O4 quantiser applied to the same bf16 q."""
+    c, sc = O.quant_fp8(O.bf16_bits_to_f32(wl.q_bits))
+    return O.dequant_fp8(c, sc)
+
+
+PREFILL_CASES = [
+    # scale of the chunked-prefill workload, block size
+    (0.02, 64),
+    (0.05, 32),
+    (0.1, 64),
+]
+
+
+@pytest.mark.parametrize("scale,bs", PREFILL_CASES)
+def test_prefill_fp8_scores_match_oracle(scale, bs):
+    wl = gen.config(4, scale=scale, block_size=bs)
+    g = GpuWorkload(wl)
+    g.quantise_q()
+    got = gpu_scores(g, fp8_q=True)
+    o = oracle_scores(wl, OracleKeys(wl), q64=oracle_fp8_q(wl))
+    print(check_scores(got, o, wl.row_len, RTOL["fp8"]))
+
+
+def test_prefill_kernel_rows_of_different_sequences():
+    # fp8 queries on the decode layout: every row reads its own sequence, so each
+    # wave of the prefill kernel makes one pass per row
+    wl = gen.config(2, scale=0.05)
+    g = GpuWorkload(wl)
+    g.store_new()
+    g.quantise_q()
+    got = gpu_scores(g, fp8_q=True)
+    ok = OracleKeys(wl)
+    o = oracle_scores(wl, ok, q64=oracle_fp8_q(wl))
+    check_scores(got, o, wl.row_len, RTOL["fp8"], slack=ok.slack())
+
+
+def test_prefill_ragged_row_count():
+    # a row count that leaves the last workgroup with partial waves
+    wl = gen.make([900], key_dtype="fp8", k=64, needle_depth=None, prefill_rows=13, seed=7)
+    g = GpuWorkload(wl)
+    g.quantise_q()
+    got = gpu_scores(g, fp8_q=True)
+    check_scores(got, oracle_scores(wl, OracleKeys(wl), q64=oracle_fp8_q(wl)), wl.row_len, RTOL["fp8"])

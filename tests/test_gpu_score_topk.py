@@ -120,3 +120,18 @@ def test_long_decode_b4_full_size():
     ok = OracleKeys(wl)
     o = oracle_scores(wl, ok)
     print(check_selection(sel, o, wl.row_len, wl.k, RTOL["fp8"], slack=ok.slack()))
+
+
+@pytest.mark.parametrize("scale", [0.05, 1.0])
+def test_prefill_fused_selection(scale):
+    """Chunked prefill: fp8 queries, 4096 (or fewer) causal rows on a 32K prefix."""
+    wl = gen.config(4, scale=scale)
+    g = GpuWorkload(wl)
+    g.quantise_q()
+    sel, sc = fused(g, fp8_q=True)
+    c, s = O.quant_fp8(O.bf16_bits_to_f32(wl.q_bits))
+    q64 = O.dequant_fp8(c, s)
+    # the oracle scores a sample of rows (every row at small scale)
+    rows = np.arange(wl.rows) if wl.rows <= 256 else np.linspace(0, wl.rows - 1, 48).astype(int)
+    o = oracle_scores(wl, OracleKeys(wl), rows=rows, q64=q64[rows])
+    print(check_selection(sel[rows], o, wl.row_len[rows], wl.k, RTOL["fp8"]))
