@@ -53,6 +53,10 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built: run `python -m sparse_attention_token_store_amd.build`")
+    try:  # bind to the HIP runtime torch has loaded (torch ships its own copy)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, i64, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                   ctypes.c_float, ctypes.c_size_t)

@@ -9,7 +9,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/dsa_indexer.h"
+#include "dsa_indexer.h"
 #include "launch.hpp"
 
 namespace {

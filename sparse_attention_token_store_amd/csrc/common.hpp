@@ -79,6 +79,23 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows that hold the
+// same column of a 16x16 MFMA accumulator), with the gfx950 row-swap permutes:
+// permlane16_swap(x, x) yields the pair (x of rows 0,0,2,2 ; x of rows 1,1,3,3), and
+// permlane32_swap the pair (halves 0,0 ; halves 1,1).  Pure VALU, no LDS round trip.
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// max(x, 0) on the bit pattern: non-negative floats order like signed integers and
+// every negative float (including -0) is a negative integer, so one v_max_i32 gives
+// the ReLU with +0 for every non-positive input.  (fmaxf would first canonicalise
+// its operand in IEEE mode, a second instruction.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 
 // number of set bits of `mask` below this lane

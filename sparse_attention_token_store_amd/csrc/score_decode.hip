@@ -175,9 +175,8 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) part = fmaf(wv[mt][v], fmaxf(acc[mt][v], 0.0f), part);
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
+          for (int v = 0; v < 4; ++v) part = fmaf(wv[mt][v], relu(acc[mt][v]), part);
+        part = rows4_sum(part);
         if constexpr (kFp8) part *= cur.s[g];
         if ((lane >> 4) == g) val = part + 0.0f;  // +0.0f: a zero score is +0
       }
