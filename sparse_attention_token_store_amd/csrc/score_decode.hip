@@ -193,6 +193,168 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 keys: the same tiling, with the key stream moved to LDS DMA.  Each wave owns
+// a ring of kRing 16-key group slots in LDS and keeps kRing-1 groups in flight with
+// global_load_lds (no VGPRs held by loads in flight), so far more bytes are
+// outstanding per wave than a register double buffer allows at 2 waves per SIMD.
+// Every group issues exactly 3 loads (2 x 1 KB of codes, 64 B of scales), so a
+// fixed vmcnt wait guarantees the group about to be read has landed; the score
+// stores interleaved with the loads only make that wait stricter.  Within a slot,
+// code chunk c of key r sits at position r*8 + (c ^ ((r >> 1) & 7)): the 16 lanes
+// of a 16-byte read phase (16 keys, same chunk) then hit 16 distinct bank groups.
+constexpr int kGroupCodes = 16 * 128;
+constexpr int kGroupSlot = kGroupCodes + 16 * 4;  // 2112 bytes
+#ifndef DSA_DECODE_RING
+#define DSA_DECODE_RING 3
+#endif
+constexpr int kDecodeRing = DSA_DECODE_RING;  // LDS slots per wave
+
+template <int BS>
+__device__ __forceinline__ void issue_group(uint8_t* slot, const uint8_t* cache, int phys, int p0, int lane) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const uint8_t* blk = cache + (int64_t)phys * (BS * 132);
+  const int off = p0 % BS;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sidx = j * 64 + lane, r = sidx >> 3, c = (sidx & 7) ^ ((r >> 1) & 7);
+    __builtin_amdgcn_global_load_lds(blk + (off + r) * 128 + c * 16,
+                                     (lds_void*)(slot + j * 1024), 16, 0, 0);
+  }
+  if (lane < 16)
+    __builtin_amdgcn_global_load_lds(blk + BS * 128 + (off + lane) * 4, (lds_void*)(slot + kGroupCodes), 4, 0, 0);
+}
+
+template <int BS, int kRing>
+__global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
+    int64_t num_blocks, const int32_t* __restrict__ block_table, int max_blocks, int num_seqs,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_len, int max_row_len,
+    float* __restrict__ scores, int64_t ld, int spans_per_wave, int write_pad) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kGroupSlot];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = blockIdx.y;
+  const int seq = row_seq[r];
+  const int n = min(max(row_len[r], 0), max_row_len);
+  float* out = scores + (int64_t)r * ld;
+  const int chunk0 = blockIdx.x * (4 * spans_per_wave * kSpan);
+  const bool seq_bad = seq < 0 || seq >= num_seqs;
+
+  if (chunk0 >= n || seq_bad) {  // nothing to read: padding, or NaN for a bad sequence
+    const int end = min(chunk0 + 4 * spans_per_wave * kSpan, max_row_len);
+    for (int p = chunk0 + (int)threadIdx.x; p < end; p += 256) {
+      if (p < n) out[p] = __builtin_nanf("");
+      else if (write_pad) out[p] = -INFINITY;
+    }
+    return;
+  }
+  const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
+  // this wave's spans: chunk0 + (i*4 + wave)*64, i < spans_per_wave; groups t = 4i + g
+  auto group_pos = [&](int t) { return chunk0 + ((t >> 2) * 4 + wave) * kSpan + 16 * (t & 3); };
+  int ngroups = 0;  // the real groups are a prefix: positions grow with t
+  while (ngroups < 4 * spans_per_wave && group_pos(ngroups) < n) ++ngroups;
+
+  // lane j holds the physical block of group j; block 0 stands in for a bad entry
+  // (whose scores become NaN) and for groups past the wave's work (loaded, never read)
+  int my_phys = 0;
+  bool my_bad = false;
+  if (lane < ngroups) {
+    const int ph = bt_row[group_pos(lane) / BS];
+    my_bad = ph < 0 || ph >= num_blocks;
+    my_phys = my_bad ? 0 : ph;
+  }
+  const uint64_t bad_groups = __ballot(my_bad);
+
+  uint8_t (*my)[kGroupSlot] = ring[wave];
+#pragma unroll
+  for (int t = 0; t < kRing - 1; ++t)
+    issue_group<BS>(my[t], cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
+
+  // A operands: head 16*mt + lane%16, dims 32*(lane/16) + 8*s .. +7
+  bf16x8_t qa[4][4];
+  {
+    const uint16_t* qr = q + (int64_t)r * 64 * kHeadDim;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        qa[mt][s4] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            qr + (16 * mt + (lane & 15)) * kHeadDim + 32 * (lane >> 4) + 8 * s4));
+  }
+  float wv[4][4];  // weights of the accumulator rows: head 16*mt + 4*(lane/16) + v
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wv[mt][v] = w[(int64_t)r * 64 + 16 * mt + 4 * (lane >> 4) + v];
+
+  // read positions of this lane in a slot: key lane%16, chunks 2*(lane/16) and +1
+  const int kr = lane & 15;
+  const int sw = (kr >> 1) & 7;
+  const int rd0 = kr * 128 + (((2 * (lane >> 4)) ^ sw) << 4);
+  const int rd1 = kr * 128 + (((2 * (lane >> 4) + 1) ^ sw) << 4);
+
+  float val = 0.0f;
+  bool bad = false;
+  int wslot = kRing - 1, rslot = 0;
+  for (int t = 0; t < ngroups; ++t) {
+    const int tn = t + kRing - 1;  // (readlane of a lane >= ngroups gives block 0)
+    issue_group<BS>(my[wslot], cache, __builtin_amdgcn_readlane(my_phys, tn & 63), group_pos(tn), lane);
+    wslot = wslot == kRing - 1 ? 0 : wslot + 1;
+    // wait for group t (3 loads x (kRing - 1) newer groups may stay in flight), then
+    // read this lane's two code chunks and its key's scale; the waits sit in the asm
+    // because the compiler would otherwise drain every load before any LDS read
+    const uint32_t sbase = (uint32_t)(uintptr_t)my[rslot];
+    rslot = rslot == kRing - 1 ? 0 : rslot + 1;
+    uint4 c0, c1;
+    float ks;
+    __asm__ volatile(
+        "s_waitcnt vmcnt(%6)\n\t"
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %4\n\t"
+        "ds_read_b32 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(c0), "=v"(c1), "=v"(ks)
+        : "v"(sbase + rd0), "v"(sbase + rd1), "v"(sbase + kGroupCodes + 4 * kr), "n"(3 * (kRing - 1))
+        : "memory");
+    const int p0 = group_pos(t);
+    bad = bad || ((bad_groups >> t) & 1);
+    f32x4_t acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const uint4 c = (s4 >> 1) ? c1 : c0;
+      const bf16x8_t b = (s4 & 1) ? fp8x8_to_bf16x8(c.z, c.w) : fp8x8_to_bf16x8(c.x, c.y);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s4], b, acc[mt], 0, 0, 0);
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part = fmaf(wv[mt][v], relu(acc[mt][v]), part);
+    part = rows4_sum(part) * ks;
+    if ((lane >> 4) == (t & 3)) val = part + 0.0f;  // +0.0f: a zero score is +0
+    if ((t & 3) == 3 || t + 1 == ngroups) {  // end of a span: one coalesced store
+      const int p = (p0 & ~(kSpan - 1)) + lane;
+      float v = val;
+      if (bad) v = __builtin_nanf("");
+      if (p >= n) v = -INFINITY;
+      if (p < max_row_len) out[p] = v;
+      val = 0.0f;
+      bad = false;
+    }
+  }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the ring before the wave ends
+  if (write_pad)  // this wave's spans past the row's keys
+    for (int i = 0; i < spans_per_wave; ++i) {
+      const int p = chunk0 + (i * 4 + wave) * kSpan + lane;
+      if (p - lane >= n && p < max_row_len) out[p] = -INFINITY;
+    }
+}
+
 template <bool kFp8>
 hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const Rows& r,
                      float* scores, int64_t ld, bool write_pad, hipStream_t s) {
@@ -203,6 +365,17 @@ hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const R
   spw = spw < 1 ? 1 : (spw > 8 ? 8 : spw);
   const int64_t per_wg = 4LL * spw;
   const dim3 grid((unsigned)((spans_row + per_wg - 1) / per_wg), (unsigned)r.rows), block(256);
+  if constexpr (kFp8) {
+    if (c.block_size == 64)
+      hipLaunchKernelGGL((score_decode_fp8_kernel<64, kDecodeRing>), grid, block, 0, s, q, w, c.base,
+                         c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
+                         r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
+    else
+      hipLaunchKernelGGL((score_decode_fp8_kernel<32, kDecodeRing>), grid, block, 0, s, q, w, c.base,
+                         c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
+                         r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
+    return hipGetLastError();
+  }
   if (c.block_size == 64)
     hipLaunchKernelGGL((score_decode_kernel<kFp8, 64>), grid, block, 0, s, q, w, c.base,
                        c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,

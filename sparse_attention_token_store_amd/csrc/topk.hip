@@ -4,21 +4,23 @@
 // isolated": the per-row top-k must agree exactly with torch.topk).
 //
 // Exact selection on order-preserving 32-bit keys, one 1024-thread workgroup per
-// chunk of up to 36,864 elements held in registers (cyclic layout: element
-// j*1024 + t lives in thread t, slot j):
+// chunk of up to 36,864 elements held in registers.  Thread t holds, for each
+// group g < R/4, the four consecutive elements g*4096 + 4t .. +3 (one 16-byte load),
+// so every position-ordered scan runs once per group of four, on packed counts.
 //  1. Lower bound.  With k <= 1024 the threads are split into >= k groups; every
 //     group owns a key >= its group maximum, so the smallest group maximum t_lo has
 //     at least k keys at or above it and the k-th largest key tau >= t_lo.  Keys
-//     below t_lo (typically 85-95% of a row) take no further part in the search.
-//  2. One histogram pass (LDS, <= 2048 bins) over the keys >= t_lo, on the 11 bits
-//     just below the common prefix of t_lo and the row maximum, where the
-//     candidates actually differ; a single wavefront scans the bins from the top to
-//     find the bin holding the k-th key.
-//  3. The keys of that bin are gathered into LDS and their low bits resolved with
-//     one or two more histogram passes over that short list (or, when a long run
-//     of ties fills the bin, with passes over the registers).
-//  4. Every key above tau is kept plus the lowest-position keys equal to it,
-//     compacted in position order with wave ballots and one scan.
+//     below t_lo (typically 80-90% of a row) take no further part.
+//  2. The live keys (>= t_lo) are compacted, in position order, into an LDS list
+//     with their positions.  (If they do not fit, e.g. long runs of equal scores,
+//     the same steps run over the registers instead.)
+//  3. Radix search for tau: an LDS histogram of up to 2048 bins over the 11 bits
+//     just below the common prefix of t_lo and the row maximum, where the live keys
+//     actually differ, then 11 bits at a time below, until the bin holding the k-th
+//     key is settled; one wavefront scans the bins from the top.
+//  4. Every key above tau is kept plus the first `rem` keys equal to it: with
+//     position-ordered counts G (greater) and E (equal) of the keys before a key,
+//     its output slot is G + min(E, rem).
 // Rows longer than one chunk are reduced level by level: each chunk keeps its own
 // top-k (exact: an element of the row's top-k under the order (score desc,
 // position asc) is also in its chunk's top-k), the survivors stay in position
@@ -36,7 +38,8 @@ constexpr int kLevelNChunk = 32768;    // later reducing levels (R = 32)
 constexpr int kMaxR = 36;
 constexpr int kMaxSingle = kMaxR * kThreads;   // 36,864: one chunk
 constexpr uint32_t kMinKey = 1u << 21;  // smallest key a real element may take
-constexpr int kCandMax = 4096;          // boundary-bin keys gathered into LDS
+constexpr int kListMax = 8192;          // live keys held in the LDS list
+constexpr int kRankMax = 128;           // boundary bins this small are settled by ranking
 
 // number of candidates a row keeps after one level with chunk size C
 __device__ __host__ __forceinline__ int64_t after_level(int64_t n, int64_t C, int k) {
@@ -44,7 +47,7 @@ __device__ __host__ __forceinline__ int64_t after_level(int64_t n, int64_t C, in
   return full * (k < C ? k : C) + (rest < k ? rest : k);
 }
 
-struct Lists {  // candidate lists of one level: keys and positions, [rows][cap]
+struct Lists {  // candidate lists of one level: keys and positions, [rows][cap], cap % 4 == 0
   uint32_t* keys;
   int32_t* idx;
   int64_t cap;
@@ -54,15 +57,31 @@ struct LevelChunks {  // chunk size of every level, passed by value
   int64_t c[8];
 };
 
+// Inclusive scan over the 64 lanes of a wavefront with the gfx9 DPP row shifts:
+// shifts by 1, 2, 4, 8 within each row of 16 lanes, then row_bcast:15 carries row
+// 0's and row 2's last lane into rows 1 and 3, and row_bcast:31 carries lane 31
+// into rows 2 and 3.  Lanes without a source take the identity.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t x, uint32_t id, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+// inclusive prefix sum over the lanes (unsigned: packed counts)
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  return wave_scan_dpp(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m));
-  return v;
+  v = wave_scan_dpp(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m));
-  return v;
+  v = wave_scan_dpp(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Run by one wavefront: find the bin (of nbins = 64 * PER, or fewer when PER = 1)
@@ -91,12 +110,7 @@ __device__ __forceinline__ void find_bin_t(const int* hist, int nbins, int rem, 
   int cnt = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) cnt += h[q];
-  int x = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = (int)wave_incl_scan((uint32_t)cnt);
   const int excl = x - cnt;
   if (has && excl < rem && x >= rem) {
     int above = excl, bin = -1, hb = 0;
@@ -128,22 +142,48 @@ __device__ __forceinline__ void find_bin(const int* hist, int nbins, int rem, in
   }
 }
 
+// One wavefront turns the per-(group, wave) packed counts tab[0..E) into exclusive
+// offsets in position order (group-major, then wave) and stores the sum in *total.
+__device__ __forceinline__ void scan_table(uint32_t* tab, int E, uint32_t* total) {
+  const int lane = lane_id();
+  const int per = (E + 63) / 64, e0 = lane * per;
+  uint32_t sum = 0;
+  for (int q = 0; q < per; ++q)
+    if (e0 + q < E) sum += tab[e0 + q];
+  const uint32_t incl = wave_incl_scan(sum);
+  uint32_t run = incl - sum;
+  for (int q = 0; q < per; ++q)
+    if (e0 + q < E) {
+      const uint32_t v = tab[e0 + q];
+      tab[e0 + q] = run;
+      run += v;
+    }
+  if (lane == 63) *total = incl;
+}
+
 // kFirst: source is the score matrix; else a candidate list.  kLast: write the
-// final out_idx / out_scores; else the next candidate list.
+// final out_idx / out_scores; else the next candidate list.  vec: 16-byte loads of
+// the source are aligned (score rows with ld % 4 == 0; lists always).
 template <int R, bool kFirst, bool kLast>
 __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     const float* __restrict__ scores, int64_t ld, Lists src, Lists dst,
     const int32_t* __restrict__ row_len, int max_row_len, int k, int nlevel, LevelChunks chunks,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_scores) {
-  constexpr int C = R * kThreads;
-  constexpr int E = R * kWaves;  // (slot, wave) entries of the compaction
+    int32_t* __restrict__ out_idx, float* __restrict__ out_scores, int vec) {
+  static_assert(R % 4 == 0, "slots come in groups of four");
+  constexpr int G = R / 4;             // groups of four per thread
+  constexpr int C = R * kThreads;      // chunk length
+  constexpr int E = G * kWaves;        // (group, wave) entries of the ordered scans
   __shared__ __attribute__((aligned(16))) int hist[2048];
-  __shared__ uint32_t cand[kCandMax];
-  __shared__ int cnt_gt[E];
-  __shared__ int cnt_eq[E];
+  __shared__ uint32_t lkey[kListMax];
+  __shared__ int32_t lpos[kListMax];
+  __shared__ uint32_t tab[E];
+  __shared__ uint32_t wtot[kWaves];
   __shared__ uint32_t red_max[kWaves], red_min[kWaves];
   __shared__ int info[3];
+  __shared__ uint32_t total;
   __shared__ int ncand;
+  __shared__ uint32_t tau_key;
+  __shared__ int tau_gt;
 
   const int r = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -162,25 +202,45 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   }
   if (nc <= 0) return;
 
+  // element 4*g + e of this thread sits at chunk offset li(g, e)
+  auto li_of = [&](int g, int e) { return g * 4 * kThreads + 4 * tid + e; };
+
   // Slots past the chunk's end hold the sentinel key 0; real keys are clamped to
   // >= 2^21 (this only touches negative-NaN bit patterns) and the lower bound is
   // never below 2^21, so the sentinel is never counted or selected.
   uint32_t key[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int li = j * kThreads + tid;
-    key[j] = 0u;
-    if (li < nc) {
-      uint32_t kv;
-      if constexpr (kFirst)
-        kv = order_key(scores[(int64_t)r * ld + base + li]);
-      else
-        kv = src.keys[(int64_t)r * src.cap + base + li];
-      key[j] = kv < kMinKey ? kMinKey : kv;
+  for (int g = 0; g < G; ++g) {
+    const int l0 = li_of(g, 0);
+    uint32_t kv[4] = {0u, 0u, 0u, 0u};
+    if (l0 < nc) {
+      if constexpr (kFirst) {
+        const float* p = scores + (int64_t)r * ld + base + l0;
+        if (vec) {
+          const float4 v = *reinterpret_cast<const float4*>(p);
+          kv[0] = order_key(v.x);
+          kv[1] = order_key(v.y);
+          kv[2] = order_key(v.z);
+          kv[3] = order_key(v.w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv[e] = l0 + e < nc ? order_key(p[e]) : 0u;
+        }
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(src.keys + (int64_t)r * src.cap + base + l0);
+        kv[0] = v.x;
+        kv[1] = v.y;
+        kv[2] = v.z;
+        kv[3] = v.w;
+      }
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[4 * g + e] = l0 + e < nc ? max(kv[e], kMinKey) : 0u;
   }
 
   auto emit = [&](int pos, int li, uint32_t kv) {
+    // (never taken: exactly k keys are selected, each from this chunk)
+    if ((unsigned)pos >= (unsigned)k || (unsigned)li >= (unsigned)nc) return;
     int32_t idx;
     if constexpr (kFirst)
       idx = (int32_t)(base + li);
@@ -199,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   if (nc <= k) {  // everything survives, in order
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const int li = j * kThreads + tid;
+      const int li = li_of(j >> 2, j & 3);
       if (li < nc) emit(li, li, key[j]);
     }
     return;
@@ -211,9 +271,9 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   for (int j = 0; j < R; ++j) tmax = max(tmax, key[j]);
   uint32_t gmax = tmax;
   if (k <= kThreads) {
-    int g = 1;  // lanes per group: the largest power of two <= 64 leaving >= k groups
-    while (g < 64 && kThreads / (2 * g) >= k) g *= 2;
-    for (int m = 1; m < g; m <<= 1) gmax = max(gmax, (uint32_t)__shfl_xor((int)gmax, m));
+    int gl = 1;  // lanes per group: the largest power of two <= 64 leaving >= k groups
+    while (gl < 64 && kThreads / (2 * gl) >= k) gl *= 2;
+    for (int m = 1; m < gl; m <<= 1) gmax = max(gmax, (uint32_t)__shfl_xor((int)gmax, m));
   }
   {
     const uint32_t wmax = wave_max_u32(tmax), wmin = wave_min_u32(gmax);
@@ -221,9 +281,8 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
       red_max[wave] = wmax;
       red_min[wave] = wmin;
     }
+    if (tid == 0) ncand = 0;
   }
-  for (int b = tid; b < 2048; b += kThreads) hist[b] = 0;
-  if (tid == 0) ncand = 0;
   __syncthreads();
   uint32_t M = 0u, tlo = 0xFFFFFFFFu;
 #pragma unroll
@@ -234,138 +293,177 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   if (k > kThreads) tlo = kMinKey;
   tlo = max(tlo, kMinKey);
 
-  // ---- 2./3. radix search for tau among keys >= t_lo
+  // ---- 2. position-ordered count of the live keys; list them in LDS if they fit
+  uint32_t lex[G];  // exclusive prefix of this lane's live count in its (group, wave)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cnt += key[4 * g + e] >= tlo ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan(cnt);
+    lex[g] = incl - cnt;
+    if (lane == 63) tab[g * kWaves + wave] = incl;
+  }
+  __syncthreads();
+  if (wave == 0) scan_table(tab, E, &total);
+  __syncthreads();
+  const int L = (int)total;
+  const bool in_lds = L <= kListMax;
+  if (in_lds) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      int at = (int)(tab[g * kWaves + wave] + lex[g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (key[4 * g + e] >= tlo && (unsigned)at < (unsigned)kListMax) {
+          lkey[at] = key[4 * g + e];
+          lpos[at] = li_of(g, e);
+          ++at;
+        }
+    }
+  }
+  // list items of this thread in list mode: [i0, i1), contiguous, in position order
+  const int per = (L + kThreads - 1) / kThreads;
+  const int i0 = min(L, tid * per), i1 = min(L, i0 + per);
+
+  // ---- 3. radix search for tau among the live keys
   uint32_t prefix, pmask;
   int rem = k;
-  if (tlo >= M) {  // every counted key equals the maximum
+  for (int b = tid; b < 2048; b += kThreads) hist[b] = 0;
+  __syncthreads();  // (also orders the list writes before the list reads)
+  if (tlo >= M) {  // every live key equals the maximum
     prefix = M;
     pmask = 0xFFFFFFFFu;
   } else {
     const int hi = 31 - __clz(tlo ^ M);
-    const int s1 = hi >= 10 ? hi - 10 : 0;
-    const int nb1 = hi - s1 + 1;
-    const uint32_t dm1 = (1u << nb1) - 1u;
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (key[j] >= tlo) atomicAdd(&hist[(key[j] >> s1) & dm1], 1);
-    __syncthreads();
-    if (wave == 0) find_bin(hist, 1 << nb1, rem, info);
-    __syncthreads();
-    const int b1 = info[0], h1 = info[2];
-    rem -= info[1];
-    const uint32_t hmask = hi >= 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
-    prefix = (M & hmask) | ((uint32_t)b1 << s1);
-    pmask = hmask | (dm1 << s1);
-    if (h1 != rem && s1 > 0) {
-      const bool in_lds = h1 <= kCandMax;
-      if (in_lds) {
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          const bool cnd = key[j] >= tlo && (key[j] & pmask) == prefix;
-          const uint64_t bm = __ballot(cnd);
-          if (bm) {
-            int at = 0;
-            if (lane == 0) at = atomicAdd(&ncand, __popcll(bm));
-            at = __shfl(at, 0);
-            if (cnd) cand[at + lanes_below(bm)] = key[j];
-          }
-        }
-      }
-      int s = s1;
-      while (s > 0) {  // uniform
-        const int ns = s >= 11 ? s - 11 : 0;
-        const int nb = s - ns;
-        const uint32_t dm = (1u << nb) - 1u;
+    int s = hi >= 10 ? hi - 10 : 0;
+    int nb = hi - s + 1;
+    // bits above `hi` are common to every live key
+    pmask = hi >= 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
+    prefix = M & pmask;
+    bool first = true;
+    while (true) {  // uniform
+      const uint32_t dm = (1u << nb) - 1u;
+      if (!first) {
         for (int b = tid; b < (1 << nb); b += kThreads) hist[b] = 0;
         __syncthreads();
-        if (in_lds) {
-          for (int q = tid; q < h1; q += kThreads) {
-            const uint32_t kv = cand[q];
-            if ((kv & pmask) == prefix) atomicAdd(&hist[(kv >> ns) & dm], 1);
-          }
-        } else {
+      }
+      if (in_lds) {
+        for (int i = i0; i < i1; ++i) {
+          const uint32_t kv = lkey[i];
+          if ((kv & pmask) == prefix) atomicAdd(&hist[(kv >> s) & dm], 1);
+        }
+      } else {
 #pragma unroll
-          for (int j = 0; j < R; ++j)
-            if (key[j] >= tlo && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> ns) & dm], 1);
+        for (int j = 0; j < R; ++j)
+          if (key[j] >= tlo && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> s) & dm], 1);
+      }
+      __syncthreads();
+      if (wave == 0) find_bin(hist, 1 << nb, rem, info);
+      __syncthreads();
+      const int bsel = info[0], hb = info[2];
+      rem -= info[1];
+      prefix |= (uint32_t)bsel << s;
+      pmask |= dm << s;
+      if (hb == rem || s == 0) break;  // the whole bin is selected, or tau is found
+      if (in_lds && hb <= kRankMax) {
+        // few keys share the boundary bin: gather them (into the histogram's
+        // space, free now) and rank each against the others; the key with
+        // gt < rem <= ge keys above or equal to it within the bin is tau
+        uint32_t* cand = reinterpret_cast<uint32_t*>(hist);
+        for (int i = i0; i < i1; ++i) {
+          const uint32_t kv = lkey[i];
+          if ((kv & pmask) == prefix) {
+            const int at = atomicAdd(&ncand, 1);
+            if (at < kRankMax) cand[at] = kv;
+          }
         }
         __syncthreads();
-        if (wave == 0) find_bin(hist, 1 << nb, rem, info);
+        if (tid < hb) {
+          const uint32_t kv = cand[tid];
+          int gt = 0, ge = 0;
+          for (int j = 0; j < hb; ++j) {
+            const uint32_t o = cand[j];
+            gt += o > kv ? 1 : 0;
+            ge += o >= kv ? 1 : 0;
+          }
+          if (gt < rem && rem <= ge) {  // (equal keys agree on both values)
+            tau_key = kv;
+            tau_gt = gt;
+          }
+        }
         __syncthreads();
-        const int b = info[0], hb = info[2];
-        rem -= info[1];
-        prefix |= (uint32_t)b << ns;
-        pmask |= dm << ns;
-        s = ns;
-        if (hb == rem) break;  // the whole bin is selected
+        prefix = tau_key;
+        pmask = 0xFFFFFFFFu;
+        rem -= tau_gt;
+        break;
       }
+      const int ns = s >= 11 ? s - 11 : 0;
+      nb = s - ns;
+      s = ns;
+      first = false;
     }
   }
 
-  // ---- 4. compaction in position order: keys above the threshold, then the first
-  // `rem` keys equal to it (only keys >= t_lo take part)
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const bool live = key[j] >= tlo;
-    const uint32_t mk = key[j] & pmask;
-    const uint64_t bgt = __ballot(live && mk > prefix);
-    const uint64_t beq = __ballot(live && mk == prefix);
-    if (lane == 0) {
-      cnt_gt[j * kWaves + wave] = __popcll(bgt);
-      cnt_eq[j * kWaves + wave] = __popcll(beq);
+  // ---- 4. emit: keys above the threshold, then the first `rem` keys equal to it;
+  // a key's output slot is (# greater before it) + min(# equal before it, rem).
+  // Counts are packed as greater | equal << 16 (each below 2^16).
+  if (in_lds) {
+    uint32_t cnt = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t mk = lkey[i] & pmask;
+      cnt += mk > prefix ? 1u : (mk == prefix ? (1u << 16) : 0u);
     }
-  }
-  __syncthreads();
-  if (wave == 0) {  // exclusive scans over the (slot, wave) entries, in position order
-    constexpr int per = (E + 63) / 64;
-    const int e0 = lane * per;
-    int se = 0;
-    for (int q = 0; q < per; ++q)
-      if (e0 + q < E) se += cnt_eq[e0 + q];
-    int xe = se;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(xe, o);
-      if (lane >= o) xe += y;
-    }
-    int run_eq = xe - se, take_sum = 0;
-    for (int q = 0; q < per; ++q)
-      if (e0 + q < E) {
-        const int ce = cnt_eq[e0 + q];
-        take_sum += cnt_gt[e0 + q] + min(max(rem - run_eq, 0), ce);
-        run_eq += ce;
+    const uint32_t incl = wave_incl_scan(cnt);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    uint32_t before = incl - cnt;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    int gtb = (int)(before & 0xFFFFu), eqb = (int)(before >> 16);
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t kv = lkey[i], mk = kv & pmask;
+      if (mk > prefix) {
+        emit(gtb + min(eqb, rem), lpos[i], kv);
+        ++gtb;
+      } else if (mk == prefix) {
+        if (eqb < rem) emit(gtb + eqb, lpos[i], kv);
+        ++eqb;
       }
-    int xs = take_sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(xs, o);
-      if (lane >= o) xs += y;
     }
-    int run_sel = xs - take_sum;
-    run_eq = xe - se;
-    for (int q = 0; q < per; ++q)
-      if (e0 + q < E) {
-        const int ce = cnt_eq[e0 + q], cg = cnt_gt[e0 + q];
-        const int t = cg + min(max(rem - run_eq, 0), ce);
-        cnt_eq[e0 + q] = run_eq;
-        cnt_gt[e0 + q] = run_sel;
-        run_eq += ce;
-        run_sel += t;
-      }
-  }
-  __syncthreads();
+  } else {
+    uint32_t gex[G];
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int li = j * kThreads + tid;
-    const bool live = key[j] >= tlo;
-    const uint32_t mk = key[j] & pmask;
-    const bool gt = live && mk > prefix;
-    const bool eq = live && mk == prefix;
-    const uint64_t bany = __ballot(gt || eq);
-    if (bany) {
-      const uint64_t beq = __ballot(eq);
-      const bool sel = gt || (eq && cnt_eq[j * kWaves + wave] + lanes_below(beq) < rem);
-      const uint64_t bsel = __ballot(sel);
-      if (sel) emit(cnt_gt[j * kWaves + wave] + lanes_below(bsel), li, key[j]);
+    for (int g = 0; g < G; ++g) {
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kv = key[4 * g + e], mk = kv & pmask;
+        const bool live = kv >= tlo;
+        cnt += live && mk > prefix ? 1u : (live && mk == prefix ? (1u << 16) : 0u);
+      }
+      const uint32_t incl = wave_incl_scan(cnt);
+      gex[g] = incl - cnt;
+      if (lane == 63) tab[g * kWaves + wave] = incl;
+    }
+    __syncthreads();
+    if (wave == 0) scan_table(tab, E, &total);
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t before = tab[g * kWaves + wave] + gex[g];
+      int gtb = (int)(before & 0xFFFFu), eqb = (int)(before >> 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kv = key[4 * g + e], mk = kv & pmask;
+        if (kv < tlo) continue;
+        if (mk > prefix) {
+          emit(gtb + min(eqb, rem), li_of(g, e), kv);
+          ++gtb;
+        } else if (mk == prefix) {
+          if (eqb < rem) emit(gtb + eqb, li_of(g, e), kv);
+          ++eqb;
+        }
+      }
     }
   }
 }
@@ -373,12 +471,12 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
 template <bool kFirst, bool kLast>
 hipError_t launch_level(int R, dim3 grid, hipStream_t s, const float* scores, int64_t ld,
                         Lists src, Lists dst, const int32_t* row_len, int max_row_len, int k,
-                        int nlevel, LevelChunks chunks, int32_t* out_idx, float* out_scores) {
+                        int nlevel, LevelChunks chunks, int32_t* out_idx, float* out_scores, int vec) {
 #define DSA_TOPK_CASE(RR)                                                                      \
   case RR:                                                                                     \
     hipLaunchKernelGGL((topk_level_kernel<RR, kFirst, kLast>), grid, dim3(kThreads), 0, s,    \
                        scores, ld, src, dst, row_len, max_row_len, k, nlevel, chunks, out_idx, \
-                       out_scores);                                                            \
+                       out_scores, vec);                                                       \
     break;
   switch (R) {
     DSA_TOPK_CASE(4)
@@ -425,13 +523,16 @@ Plan make_plan(int max_row_len, int k) {
   return p;
 }
 
+// list row stride: the longest list, rounded up to whole 16-byte loads
+int64_t list_cap(const Plan& p) { return (p.len[1] + 3) / 4 * 4; }
+
 }  // namespace
 
 // workspace: two ping-pong candidate lists (none for rows that fit one chunk)
 size_t topk_ws_bytes(int rows, int max_row_len, int k) {
   const Plan p = make_plan(max_row_len, k);
   if (p.levels == 1) return 0;
-  const int64_t cap = p.len[1];
+  const int64_t cap = list_cap(p);
   const size_t list = (size_t)rows * (size_t)cap * 8;
   return 2 * ((list + 255) / 256 * 256);
 }
@@ -444,13 +545,15 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_len, 
   Lists none{nullptr, nullptr, 0};
   LevelChunks chunks{};
   for (int l = 0; l < p.levels; ++l) chunks.c[l] = p.chunk[l];
+  // 16-byte loads of score rows when every row start is 16-byte aligned
+  const int vec = (ld % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) ? 1 : 0;
   if (p.levels == 1) {
     const int R = (int)(p.chunk[0] / kThreads);
     return launch_level<true, true>(R, dim3(1, rows), s, scores, ld, none, none, row_len,
-                                    max_row_len, k, 0, chunks, out_idx, out_scores);
+                                    max_row_len, k, 0, chunks, out_idx, out_scores, vec);
   }
   uint8_t* w8 = static_cast<uint8_t*>(ws);
-  const int64_t cap = p.len[1];
+  const int64_t cap = list_cap(p);
   const size_t list = ((size_t)rows * (size_t)cap * 8 + 255) / 256 * 256;
   Lists L[2];
   for (int i = 0; i < 2; ++i) {
@@ -467,13 +570,13 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_len, 
     const Lists dst = last ? none : L[l & 1];
     if (first)
       e = launch_level<true, false>(R, dim3(nchunks, rows), s, scores, ld, src, dst, row_len,
-                                    max_row_len, k, 0, chunks, out_idx, out_scores);
+                                    max_row_len, k, 0, chunks, out_idx, out_scores, vec);
     else if (!last)
       e = launch_level<false, false>(R, dim3(nchunks, rows), s, scores, ld, src, dst, row_len,
-                                     max_row_len, k, l, chunks, out_idx, out_scores);
+                                     max_row_len, k, l, chunks, out_idx, out_scores, 1);
     else
       e = launch_level<false, true>(R, dim3(1, rows), s, scores, ld, src, dst, row_len,
-                                    max_row_len, k, l, chunks, out_idx, out_scores);
+                                    max_row_len, k, l, chunks, out_idx, out_scores, 1);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
