@@ -160,10 +160,11 @@ class Runner:
                 "kernel": "score_decode"}
 
 
-def cpu_baseline(wl, kd, budget_s=15.0):
+def cpu_baseline(wl, kd, budget_s=15.0, min_s=10.0):
     """The oracle (numpy float64, BLAS threads as configured) on a bounded sample of
     the same workload: whole rows (store chain of the row's new tokens, key
-    dequantisation, score, top-k), as many as fit the time budget."""
+    dequantisation, score, top-k), repeated over the rows until about budget_s of
+    CPU work (at least min_s) has been timed."""
     from oracle import oracle as O
     try:
         import threadpoolctl
@@ -173,43 +174,46 @@ def cpu_baseline(wl, kd, budget_s=15.0):
     rows_done, keys_done, t_total = 0, 0, 0.0
     order = np.argsort(wl.row_len)[::-1] if wl.rows > 1 else np.arange(wl.rows)
     prefix_cache = {}
-    for r in order:
-        b = int(wl.row_seq[r])
-        n = int(wl.row_len[r])
-        if b not in prefix_cache:               # cache fill: not timed (setup)
-            x = wl.keys_bits[b]
-            if kd == "fp8":
-                prefix_cache[b] = O.quant_fp8(O.bf16_bits_to_f32(x))
-            else:
-                prefix_cache[b] = x
-        t0 = time.perf_counter()
-        sel = wl.new_seq == b
-        parts = []
-        store = prefix_cache[b]
-        nstored = int(wl.stored_len[b])
-        for p0 in range(0, min(n, nstored), 1 << 16):
-            p1 = min(n, nstored, p0 + (1 << 16))
-            parts.append(O.dequant_fp8(store[0][p0:p1], store[1][p0:p1]) if kd == "fp8"
-                         else O.bf16_bits_to_f64(store[p0:p1]))
-        if n > nstored:
-            y = O.store_chain(wl.new_x_bits[sel], wl.new_pos[sel], 7, wl.rms_eps, wl.rope_base, wl.rope_dim)
-            parts.append(O.dequant_fp8(*O.quant_fp8(y.astype(np.float32))) if kd == "fp8" else y)
-        keys = np.concatenate(parts, 0)[:n]
-        q = O.bf16_bits_to_f64(wl.q_bits[r])
-        if wl.q_dtype == "fp8":
-            c, s = O.quant_fp8(O.bf16_bits_to_f32(wl.q_bits[r]))
-            q = O.dequant_fp8(c, s)
-        sc = O.score(q, wl.w[r].astype(np.float64), keys)
-        O.topk(sc[None], [n], wl.k)
-        t_total += time.perf_counter() - t0
-        rows_done += 1
-        keys_done += n
-        if t_total >= budget_s:
-            break
+    passes = 0
+    while t_total < min_s:
+        for r in order:
+            b = int(wl.row_seq[r])
+            n = int(wl.row_len[r])
+            if b not in prefix_cache:               # cache fill: not timed (setup)
+                x = wl.keys_bits[b]
+                if kd == "fp8":
+                    prefix_cache[b] = O.quant_fp8(O.bf16_bits_to_f32(x))
+                else:
+                    prefix_cache[b] = x
+            t0 = time.perf_counter()
+            sel = wl.new_seq == b
+            parts = []
+            store = prefix_cache[b]
+            nstored = int(wl.stored_len[b])
+            for p0 in range(0, min(n, nstored), 1 << 16):
+                p1 = min(n, nstored, p0 + (1 << 16))
+                parts.append(O.dequant_fp8(store[0][p0:p1], store[1][p0:p1]) if kd == "fp8"
+                             else O.bf16_bits_to_f64(store[p0:p1]))
+            if n > nstored:
+                y = O.store_chain(wl.new_x_bits[sel], wl.new_pos[sel], 7, wl.rms_eps, wl.rope_base, wl.rope_dim)
+                parts.append(O.dequant_fp8(*O.quant_fp8(y.astype(np.float32))) if kd == "fp8" else y)
+            keys = np.concatenate(parts, 0)[:n]
+            q = O.bf16_bits_to_f64(wl.q_bits[r])
+            if wl.q_dtype == "fp8":
+                c, s = O.quant_fp8(O.bf16_bits_to_f32(wl.q_bits[r]))
+                q = O.dequant_fp8(c, s)
+            sc = O.score(q, wl.w[r].astype(np.float64), keys)
+            O.topk(sc[None], [n], wl.k)
+            t_total += time.perf_counter() - t0
+            rows_done += 1
+            keys_done += n
+            if t_total >= budget_s:
+                break
+        passes += 1
     return {"value": keys_done / t_total, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} of {wl.rows} rows ({keys_done} visible keys) of the same workload, "
-                      f"{t_total:.1f} s: store chain of the row's new tokens, fp8/bf16 key decode, "
-                      f"float64 score, sort-based top-k",
+            "sample": f"{rows_done} rows ({keys_done} visible keys; {passes} pass(es) over the "
+                      f"{wl.rows} rows of the same workload), {t_total:.1f} s: store chain of the "
+                      f"row's new tokens, fp8/bf16 key decode, float64 score, sort-based top-k",
             "selections_per_s": rows_done / t_total}
 
 

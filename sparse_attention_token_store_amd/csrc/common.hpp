@@ -98,6 +98,15 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 
+// Workgroup barrier that orders LDS only: wait for this wave's LDS operations, then
+// s_barrier.  __syncthreads() adds a workgroup-scope release fence, which on gfx9
+// drains every outstanding vector-memory load as well, so global prefetches could
+// never stay in flight across it.  The memory clobber keeps the compiler from moving
+// memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // number of set bits of `mask` below this lane
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -12,15 +12,21 @@
 //    are 2^0: the real scales are folded into the epilogue.
 //  - Workgroup = 8 waves, one query row per wave, 8 consecutive rows of one
 //    sequence.  Each wave keeps its row's 64 heads as 4 A tiles in registers.
-//  - The 8 waves share the keys through LDS: every 64-key span (8 KB of codes plus
-//    256 B of scales) is loaded once per workgroup with one 16-byte chunk per
-//    thread, prefetched two spans ahead in registers and written to a double-buffered
-//    LDS stage.  Key rows are padded to 144 bytes: 16-byte reads of 16 consecutive
-//    keys at the same offset then fall on 16 distinct bank groups (9r mod 16 is a
-//    permutation), so the B-operand reads, lane = (key, 32-byte quarter), do not
-//    conflict.  About 120 VGPRs per wave: 4 waves per SIMD hide the latency.
-//  - Within a wave the next 16-key group's LDS reads and MFMAs are issued before the
-//    current group's epilogue, so the matrix core and the VALU overlap.
+//  - The 8 waves share the keys through LDS: every stage of 256 keys (four 64-token
+//    blocks: 32 KB of codes plus 1 KB of scales) is loaded once per workgroup, four
+//    16-byte code chunks and one scale per thread, a stage ahead in registers, and
+//    copied into a double-buffered LDS stage (75 KB: two workgroups per CU).  Key rows are padded to 144 bytes:
+//    16-byte reads of 16 consecutive keys at the same offset then fall on 16
+//    distinct bank groups (9r mod 16 is a permutation), so the B-operand reads,
+//    lane = (key, 32-byte quarter), do not conflict.  A key whose block id lies
+//    outside the pool is staged with a NaN scale, so its score is NaN without any
+//    check in the scoring loop.  About 120 VGPRs per wave: 4 waves per SIMD.
+//  - The stage barrier orders LDS only (the global prefetch stays in flight across
+//    it), every thread issues the same loads each stage (positions past the last
+//    key clamped to it) so the compiler's load-counter waits stay exact, and the
+//    block-table entries are fetched a stage before the keys they locate.
+//  - The matrix core and the VALU overlap across the 4 waves of a SIMD (within one
+//    wave they largely take turns), so each 16-key group is scored in place.
 //  - Keys are split into 8 chunks and workgroup w takes chunk w mod 8.  Workgroups
 //    are dispatched to the 8 XCDs round robin, so each XCD's L2 only ever holds its
 //    eighth of the keys.
@@ -34,45 +40,71 @@
 namespace dsa {
 namespace {
 
-constexpr int kSpan = 64;
+constexpr int kSpan = 64;                   // keys per score store (one per lane)
 constexpr int kWavesPf = 8;                 // one query row per wave
 constexpr int kThreadsPf = 64 * kWavesPf;
 constexpr int kKeyChunks = 8;
-constexpr int kRowPitch = 144;                       // padded LDS key row
-constexpr int kScaleOff = kSpan * kRowPitch;          // scales after the 64 rows
-constexpr int kStage = kScaleOff + kSpan * 4;         // 9472 bytes per staged span
+constexpr int kStageKeys = 256;                         // keys per LDS stage
+constexpr int kStageGroups = kStageKeys / 16;
+constexpr int kRowPitch = 144;                          // padded LDS key row
+constexpr int kScaleOff = kStageKeys * kRowPitch;       // scales after the key rows
+constexpr int kStage = kScaleOff + kStageKeys * 4;      // 37,888 bytes per stage
 
-// One thread's share of a span: code chunk tid & 7 of key tid >> 3, and for tid < 16
-// the 16 bytes of scales of keys 4*tid .. 4*tid+3.
+// One thread's share of a stage: code chunk tid & 7 of keys 64j + (tid >> 3), j < 4,
+// and the scale of key tid % 256 (threads 0..255 stage it).  Every thread issues the
+// same loads every stage, with positions past the last key clamped to it: with no
+// skipped loads the compiler's load-counter waits stay exact.  (Keys past a row's
+// end are overwritten with -inf, so what the clamped loads bring is never used.)
+// Named fields, not arrays: an aggregate array here ends up in scratch memory.
 struct Share {
-  uint4 code;
-  uint4 scale;
+  uint4 c0, c1, c2, c3;
+  uint32_t scale;
+};
+
+// Block-table entries behind one thread's share of the stage at p0, fetched a stage
+// before the share itself so the key loads never wait on a block-table load.
+struct ShareBlocks {
+  int b0, b1, b2, b3, scale;
 };
 
 template <int BS>
-__device__ __forceinline__ void load_share(Share& sh, const uint8_t* cache, int64_t num_blocks,
-                                           const int32_t* bt_row, int p_span, int n_max, int tid) {
-  const int key = tid >> 3;
-  const int c = tid & 7;
-  const int pos = p_span + key;
-  if (pos < n_max) {
-    int phys = bt_row[pos / BS];
-    phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;
-    sh.code = *reinterpret_cast<const uint4*>(cache + (int64_t)phys * (BS * 132) + (pos % BS) * 128 + c * 16);
-  }
-  if (tid < 16) {
-    const int p4 = p_span + 4 * tid;
-    if (p4 < n_max) {
-      int phys = bt_row[p4 / BS];
-      phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;
-      sh.scale = *reinterpret_cast<const uint4*>(cache + (int64_t)phys * (BS * 132) + BS * 128 + (p4 % BS) * 4);
-    }
-  }
+__device__ __forceinline__ ShareBlocks share_blocks(const int32_t* bt_row, int p0, int n_max, int tid) {
+  const int last = n_max - 1, k = p0 + (tid >> 3);
+  return ShareBlocks{bt_row[min(k, last) / BS], bt_row[min(k + 64, last) / BS], bt_row[min(k + 128, last) / BS],
+                     bt_row[min(k + 192, last) / BS], bt_row[min(p0 + (tid & 255), last) / BS]};
+}
+
+template <int BS>
+__device__ __forceinline__ uint4 load_code(const uint8_t* cache, int64_t num_blocks, int entry, int pos, int tid) {
+  const int phys = (entry < 0 || entry >= num_blocks) ? 0 : entry;
+  return *reinterpret_cast<const uint4*>(cache + (int64_t)phys * (BS * 132) + (pos % BS) * 128 + (tid & 7) * 16);
+}
+
+template <int BS>
+__device__ __forceinline__ Share load_share(const uint8_t* cache, int64_t num_blocks, const ShareBlocks& e,
+                                            int p0, int n_max, int tid) {
+  const int last = n_max - 1, k = p0 + (tid >> 3);
+  Share sh;
+  sh.c0 = load_code<BS>(cache, num_blocks, e.b0, min(k, last), tid);
+  sh.c1 = load_code<BS>(cache, num_blocks, e.b1, min(k + 64, last), tid);
+  sh.c2 = load_code<BS>(cache, num_blocks, e.b2, min(k + 128, last), tid);
+  sh.c3 = load_code<BS>(cache, num_blocks, e.b3, min(k + 192, last), tid);
+  // a block id outside the pool stages a NaN scale: its keys score NaN
+  const int ps = min(p0 + (tid & 255), last);
+  const bool bad = e.scale < 0 || e.scale >= num_blocks;
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(cache + (int64_t)(bad ? 0 : e.scale) * (BS * 132) +
+                                                        BS * 128 + (ps % BS) * 4);
+  sh.scale = bad ? 0x7FC00000u : v;
+  return sh;
 }
 
 __device__ __forceinline__ void store_share(uint8_t* stage, const Share& sh, int tid) {
-  *reinterpret_cast<uint4*>(stage + (tid >> 3) * kRowPitch + (tid & 7) * 16) = sh.code;
-  if (tid < 16) *reinterpret_cast<uint4*>(stage + kScaleOff + tid * 16) = sh.scale;
+  uint8_t* p = stage + (tid >> 3) * kRowPitch + (tid & 7) * 16;
+  *reinterpret_cast<uint4*>(p) = sh.c0;
+  *reinterpret_cast<uint4*>(p + 64 * kRowPitch) = sh.c1;
+  *reinterpret_cast<uint4*>(p + 128 * kRowPitch) = sh.c2;
+  *reinterpret_cast<uint4*>(p + 192 * kRowPitch) = sh.c3;
+  if (tid < kStageKeys) reinterpret_cast<uint32_t*>(stage + kScaleOff)[tid] = sh.scale;
 }
 
 // B operand of group g for this lane: key 16g + lane%16, code bytes 32*(lane/16) .. +31
@@ -98,7 +130,7 @@ __device__ __forceinline__ float group_score(const f32x4_t (&acc)[4], const floa
 }
 
 template <int BS>
-__global__ __launch_bounds__(kThreadsPf, 2) void score_prefill_kernel(
+__global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ cache, int64_t num_blocks, const int32_t* __restrict__ block_table,
     int max_blocks, int num_seqs, const int32_t* __restrict__ row_seq,
@@ -168,50 +200,62 @@ __global__ __launch_bounds__(kThreadsPf, 2) void score_prefill_kernel(
     // ---- staged path: all rows read sequence s0
     const int32_t* bt_row = block_table + (int64_t)s0 * max_blocks;
     const int kend = min(k1, n_max);
-    const int nspans = kend > k0 ? (kend - k0 + kSpan - 1) / kSpan : 0;
-    Share reg[2];
-    if (nspans > 0) load_share<BS>(reg[0], cache, num_blocks, bt_row, k0, n_max, tid);
-    if (nspans > 1) load_share<BS>(reg[1], cache, num_blocks, bt_row, k0 + kSpan, n_max, tid);
-    if (nspans > 0) store_share(stage[0], reg[0], tid);
-    if (nspans > 2) load_share<BS>(reg[0], cache, num_blocks, bt_row, k0 + 2 * kSpan, n_max, tid);
-    __syncthreads();
-    for (int i = 0; i < nspans; ++i) {
-      // stage[i&1] holds span i; reg[(i+1)&1] holds span i+1; reg[i&1] span i+2
-      const uint8_t* st = stage[i & 1];
-      const int p_span = k0 + i * kSpan;
-      if (active && p_span < n) {
-        float val = 0.0f;
-        f32x4_t acc[2][4];
-        float sg[2];
-#pragma unroll
-        for (int g = 0; g <= 4; ++g) {
-          if (g < 4) {  // LDS reads and MFMAs of group g ...
-            const i32x8_t b = read_b(st, g, lane);
-            sg[g & 1] = read_scale(st, g, lane);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              acc[g & 1][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-          }
-          if (g > 0) {  // ... before the epilogue of group g-1
-            const float sc = group_score(acc[(g - 1) & 1], wq, sg[(g - 1) & 1]);
-            if ((lane >> 4) == g - 1) val = sc;
-          }
-        }
-        // a block id outside the pool makes the keys it covers NaN
-        const int p = p_span + lane;
-        const int pb = min(p, n_max - 1);
-        const int phys = bt_row[pb / BS];
-        if (phys < 0 || phys >= num_blocks) val = __builtin_nanf("");
-        if (p >= n) val = -INFINITY;
-        if (p < k1 && (p < n || write_pad)) __builtin_nontemporal_store(val, out + p);
-      } else if (active && write_pad) {
-        const int p = p_span + lane;
-        if (p < k1) __builtin_nontemporal_store(-INFINITY, out + p);
+    const int nst = kend > k0 ? (kend - k0 + kStageKeys - 1) / kStageKeys : 0;
+    if (nst == 0) {  // no key of the chunk is visible to any row
+      if (active && write_pad)
+        for (int p = k0 + lane; p < k1; p += 64) out[p] = -INFINITY;
+      return;
+    }
+    auto blocks = [&](int i) { return share_blocks<BS>(bt_row, k0 + i * kStageKeys, n_max, tid); };
+    auto share = [&](const ShareBlocks& e, int i) {
+      return load_share<BS>(cache, num_blocks, e, k0 + i * kStageKeys, n_max, tid);
+    };
+    // Scores stage i from the staged copy st: groups of 16 keys, one 64-key store
+    // per 4 groups (reads the row's operands only).
+    auto score_stage = [&](int i, const uint8_t* st) {
+      const int p0 = k0 + i * kStageKeys;
+      if (!active) return;
+      if (p0 >= n) {  // none of these keys is visible to this row
+        if (write_pad)
+          for (int p = p0 + lane; p < min(p0 + kStageKeys, k1); p += 64) __builtin_nontemporal_store(-INFINITY, out + p);
+        return;
       }
-      if (i + 1 < nspans) store_share(stage[(i + 1) & 1], reg[(i + 1) & 1], tid);
-      if (i + 3 < nspans) load_share<BS>(reg[(i + 1) & 1], cache, num_blocks, bt_row, k0 + (i + 3) * kSpan, n_max, tid);
-      __syncthreads();
+      float val = 0.0f;
+#pragma unroll
+      for (int g = 0; g < kStageGroups; ++g) {
+        const i32x8_t b = read_b(st, g, lane);
+        const float sg = read_scale(st, g, lane);
+        f32x4_t acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        const float sc = group_score(acc, wq, sg);
+        if ((lane >> 4) == (g & 3)) val = sc;
+        if ((g & 3) == 3) {  // 64 keys done: one coalesced store
+          const int p = p0 + 16 * (g - 3) + lane;
+          const float v = p >= n ? -INFINITY : val;
+          if (p < k1 && (p < n || write_pad)) __builtin_nontemporal_store(v, out + p);
+        }
+      }
+    };
+    // Iteration i copies stage i+1 (loaded during iteration i-1) from registers into
+    // the free LDS buffer, fetches stage i+3's block entries and issues stage i+2's
+    // loads into the same registers, then scores stage i.
+    Share r = share(blocks(0), 0);
+    store_share(stage[0], r, tid);
+    r = share(blocks(1), 1);
+    ShareBlocks next = blocks(2);  // block entries of stage i+2 at the top of iteration i
+    lds_barrier();
+    for (int i = 0; i < nst; ++i) {
+      if (i + 1 < nst) store_share(stage[(i + 1) & 1], r, tid);
+      {
+        const ShareBlocks e = next;
+        next = blocks(i + 3);
+        r = share(e, i + 2);
+      }
+      score_stage(i, stage[i & 1]);
+      lds_barrier();  // (the prefetched stage stays in flight)
     }
     if (active && write_pad)  // positions past every key of the workgroup
       for (int p = max(kend, k0) + lane; p < k1; p += 64) out[p] = -INFINITY;

@@ -87,18 +87,33 @@ def test_rows_sharing_a_sequence():
     check_scores(got, oracle_scores(wl, OracleKeys(wl, "bf16")), wl.row_len, RTOL["bf16"])
 
 
-def test_bad_block_id_scores_nan_without_faulting():
-    # a block id outside the pool is caught by the kernel's bounds check: the
-    # affected 16-key groups score NaN, nothing is read out of bounds
-    wl = gen.config(1, scale=0.2)
+@pytest.mark.parametrize("case", ["bf16_keys", "fp8_keys", "fp8_prefill"])
+def test_bad_block_id_scores_nan_without_faulting(case):
+    # a block id outside the pool is caught by the kernel's bounds check: the keys
+    # it covers score NaN in every row that sees them, nothing is read out of bounds
+    # (one case per scoring kernel: bf16 keys, fp8 keys, fp8 queries)
+    wl = {"bf16_keys": lambda: gen.config(1, scale=0.2),
+          "fp8_keys": lambda: gen.config(2, scale=0.05),
+          "fp8_prefill": lambda: gen.config(4, scale=0.02)}[case]()
+    seq = int(wl.row_seq[0])
     bt = wl.block_table.copy()
-    bt[0, 1] = wl.num_blocks + 5
+    bt[seq, 1] = wl.num_blocks + 5
     g = GpuWorkload(wl, block_table=bt)
-    got = gpu_scores(g)
-    n = int(wl.row_len[0])
+    if case == "fp8_prefill":
+        g.quantise_q()
+        got = gpu_scores(g, fp8_q=True)
+    else:
+        got = gpu_scores(g)
     bs = wl.block_size
-    assert np.all(np.isnan(got[0, bs:min(2 * bs, n)]))
-    assert np.all(np.isfinite(got[0, :bs]))
+    checked = 0
+    for r in range(wl.rows):
+        n = int(wl.row_len[r])
+        if int(wl.row_seq[r]) != seq or n <= bs:
+            continue
+        assert np.all(np.isnan(got[r, bs:min(2 * bs, n)]))
+        assert np.all(np.isfinite(got[r, :bs]))
+        checked += 1
+    assert checked > 0
 
 
 def test_needle_ranks_first_on_gpu_scores():
