@@ -11,18 +11,19 @@
 //    v_mfma_f32_16x16x32_bf16.  At ~8 TB/s of fp8 keys the contraction needs
 //    ~0.5 P MAC/s, far beyond the vector ALU, so it must run on the matrix cores.
 //  - Each wavefront holds the whole query row as MFMA A operands in registers
-//    (64 VGPRs) and streams its own keys straight from HBM into B-operand registers:
-//    no LDS, no cross-wave reduction.  The contraction index d is permuted so that
-//    lane l reads one contiguous 64-byte (bf16) or 32-byte (fp8) run of key
-//    l mod 16 with 16-byte loads; A uses the same permutation, so the dot products
-//    are unchanged.
+//    (64 VGPRs) and scores its own keys: no cross-wave reduction.  The contraction
+//    index d is permuted so that lane l reads one contiguous 64-byte (bf16) or
+//    32-byte (fp8) run of key l mod 16; A uses the same permutation, so the dot
+//    products are unchanged.
+//  - fp8 keys (score_decode_fp8_kernel) stream through a per-wave LDS ring filled by
+//    LDS DMA, which keeps two 16-key groups in flight without holding VGPRs
+//    (4 waves per SIMD).  bf16 keys (score_decode_kernel) load each 64-key span
+//    straight into registers with the next span prefetched.
 //  - fp8 codes are widened to bf16 exactly (every e4m3 value is a bf16 value) with
 //    v_cvt_scalef32_pk_bf16_fp8; the per-key scale multiplies the head sum.
 //  - The ReLU-weighted head sum is in-lane (16 of the 64 heads per lane) plus two
-//    cross-lane adds; lane l ends up with the score of key 16*(l/16) + l%16 of a
-//    64-key span, so each span is stored with one coalesced 256-byte write.
-//  - Software pipeline: the next span's keys are loaded before the current span is
-//    computed.
+//    cross-lane adds; lane l ends up with the score of key l%16 of its group, and
+//    64 scores at a time leave with one coalesced 256-byte write.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -374,16 +375,16 @@ hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const R
       hipLaunchKernelGGL((score_decode_fp8_kernel<32, kDecodeRing>), grid, block, 0, s, q, w, c.base,
                          c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
                          r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
-    return hipGetLastError();
+  } else {  // bf16 keys: the register-streaming kernel
+    if (c.block_size == 64)
+      hipLaunchKernelGGL((score_decode_kernel<false, 64>), grid, block, 0, s, q, w, c.base,
+                         c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
+                         r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
+    else
+      hipLaunchKernelGGL((score_decode_kernel<false, 32>), grid, block, 0, s, q, w, c.base,
+                         c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
+                         r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
   }
-  if (c.block_size == 64)
-    hipLaunchKernelGGL((score_decode_kernel<kFp8, 64>), grid, block, 0, s, q, w, c.base,
-                       c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
-                       r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
-  else
-    hipLaunchKernelGGL((score_decode_kernel<kFp8, 32>), grid, block, 0, s, q, w, c.base,
-                       c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
-                       r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
   return hipGetLastError();
 }
 
