@@ -16,8 +16,9 @@
 //     the same steps run over the registers instead.)
 //  3. Radix search for tau: an LDS histogram of up to 2048 bins over the 11 bits
 //     just below the common prefix of t_lo and the row maximum, where the live keys
-//     actually differ, then 11 bits at a time below, until the bin holding the k-th
-//     key is settled; one wavefront scans the bins from the top.
+//     actually differ; one wavefront scans the bins from the top.  A boundary bin of
+//     at most 128 keys is settled by ranking its keys against each other, otherwise
+//     11 more bits at a time.
 //  4. Every key above tau is kept plus the first `rem` keys equal to it: with
 //     position-ordered counts G (greater) and E (equal) of the keys before a key,
 //     its output slot is G + min(E, rem).
@@ -34,7 +35,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLevel0Chunk = 16384;    // first reducing level of long rows (R = 16)
-constexpr int kLevelNChunk = 32768;    // later reducing levels (R = 32)
+constexpr int kLevelNChunk = 32768;    // largest chunk of the later reducing levels (R = 32)
 constexpr int kMaxR = 36;
 constexpr int kMaxSingle = kMaxR * kThreads;   // 36,864: one chunk
 constexpr uint32_t kMinKey = 1u << 21;  // smallest key a real element may take
@@ -511,8 +512,17 @@ Plan make_plan(int max_row_len, int k) {
   int64_t n = max_row_len;
   p.len[0] = n;
   while (n > kMaxSingle) {
-    int64_t C = p.levels == 0 ? kLevel0Chunk : kLevelNChunk;
-    while (C < 2LL * k) C *= 2;  // each level must shrink the list (C <= 32768 for k <= 8192)
+    // first level: 16,384-element chunks (at least 2k); later levels: chunks of 8k
+    // (a power of two, at most 32,768), so a level keeps 1 in 8 and still spreads a
+    // few long rows over many workgroups
+    int64_t C;
+    if (p.levels == 0) {
+      C = kLevel0Chunk;
+      while (C < 2LL * k) C *= 2;  // each level must shrink the list
+    } else {
+      C = 4096;
+      while (C < 8LL * k && C < kLevelNChunk) C *= 2;  // (C >= 2k for k <= 8192)
+    }
     p.chunk[p.levels] = C;
     n = after_level(n, C, k);
     ++p.levels;
