@@ -45,6 +45,10 @@ CASES = [
     (2, 100000, 8192, "normal"),
     (3, 1000, 1, "normal"),
     (3, 1000, 7, "ties"),
+    # more live keys than the kernel's LDS list holds: the register passes
+    (2, 22000, 512, "equal"),
+    (2, 36864, 1024, "equal"),
+    (2, 30000, 1024, "increasing"),
 ]
 
 
