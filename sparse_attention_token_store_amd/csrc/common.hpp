@@ -90,6 +90,22 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Reduce-scatter over the four 16-lane rows for four 16-key groups at once.  p_g
+// holds, in lane l, a partial sum for key l%16 of group g over the heads of lane-row
+// l/16; the result in lane l is the full sum (all four rows) for key l%16 of group
+// l/16, i.e. key l of the 64-key span.  permlane32_swap(a, b) leaves
+// (a.lo, b.lo | a.hi, b.hi) so a.lo + a.hi pairs rows (0,2) and (1,3): the low half
+// keeps groups 0 and 1, the high half groups 2 and 3; one permlane16_swap then pairs
+// the remaining rows.  3 swaps and 3 adds for 64 keys.
+__device__ __forceinline__ float rows4_reduce_scatter(float p0, float p1, float p2, float p3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+  const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+  const float s13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // max(x, 0) on the bit pattern: non-negative floats order like signed integers and
 // every negative float (including -0) is a negative integer, so one v_max_i32 gives
 // the ReLU with +0 for every non-positive input.  (fmaxf would first canonicalise

@@ -31,7 +31,8 @@
 //    are dispatched to the 8 XCDs round robin, so each XCD's L2 only ever holds its
 //    eighth of the keys.
 //  - Epilogue per 16-key tile: ReLU, weight by w*qs, in-lane head sum over the 16
-//    heads a lane holds, a cross-row permute sum, per-key scale.
+//    heads a lane holds; then per 64 keys one reduce-scatter over the four lane-rows
+//    (3 permlane swaps) and one per-key scale, so lane l holds key l of the span.
 //  - A workgroup whose rows read different sequences falls back to per-wave direct
 //    loads (correct, slower; chunked prefill never takes it).
 #include "common.hpp"
@@ -67,33 +68,36 @@ struct ShareBlocks {
   int b0, b1, b2, b3, scale;
 };
 
+// (Positions are non-negative: unsigned arithmetic makes / BS and % BS shifts and masks.)
 template <int BS>
 __device__ __forceinline__ ShareBlocks share_blocks(const int32_t* bt_row, int p0, int n_max, int tid) {
-  const int last = n_max - 1, k = p0 + (tid >> 3);
-  return ShareBlocks{bt_row[min(k, last) / BS], bt_row[min(k + 64, last) / BS], bt_row[min(k + 128, last) / BS],
-                     bt_row[min(k + 192, last) / BS], bt_row[min(p0 + (tid & 255), last) / BS]};
+  const uint32_t last = (uint32_t)n_max - 1u, k = (uint32_t)p0 + ((uint32_t)tid >> 3);
+  const uint32_t ks = (uint32_t)p0 + ((uint32_t)tid & 255u);
+  return ShareBlocks{bt_row[min(k, last) / BS], bt_row[min(k + 64u, last) / BS], bt_row[min(k + 128u, last) / BS],
+                     bt_row[min(k + 192u, last) / BS], bt_row[min(ks, last) / BS]};
 }
 
 template <int BS>
-__device__ __forceinline__ uint4 load_code(const uint8_t* cache, int64_t num_blocks, int entry, int pos, int tid) {
-  const int phys = (entry < 0 || entry >= num_blocks) ? 0 : entry;
-  return *reinterpret_cast<const uint4*>(cache + (int64_t)phys * (BS * 132) + (pos % BS) * 128 + (tid & 7) * 16);
+__device__ __forceinline__ uint4 load_code(const uint8_t* cache, int64_t num_blocks, int entry, uint32_t pos, int tid) {
+  const uint32_t phys = (entry < 0 || entry >= num_blocks) ? 0u : (uint32_t)entry;
+  return *reinterpret_cast<const uint4*>(cache + (uint64_t)phys * (BS * 132) +
+                                         ((pos % BS) * 128u + ((uint32_t)tid & 7u) * 16u));
 }
 
 template <int BS>
 __device__ __forceinline__ Share load_share(const uint8_t* cache, int64_t num_blocks, const ShareBlocks& e,
                                             int p0, int n_max, int tid) {
-  const int last = n_max - 1, k = p0 + (tid >> 3);
+  const uint32_t last = (uint32_t)n_max - 1u, k = (uint32_t)p0 + ((uint32_t)tid >> 3);
   Share sh;
   sh.c0 = load_code<BS>(cache, num_blocks, e.b0, min(k, last), tid);
-  sh.c1 = load_code<BS>(cache, num_blocks, e.b1, min(k + 64, last), tid);
-  sh.c2 = load_code<BS>(cache, num_blocks, e.b2, min(k + 128, last), tid);
-  sh.c3 = load_code<BS>(cache, num_blocks, e.b3, min(k + 192, last), tid);
+  sh.c1 = load_code<BS>(cache, num_blocks, e.b1, min(k + 64u, last), tid);
+  sh.c2 = load_code<BS>(cache, num_blocks, e.b2, min(k + 128u, last), tid);
+  sh.c3 = load_code<BS>(cache, num_blocks, e.b3, min(k + 192u, last), tid);
   // a block id outside the pool stages a NaN scale: its keys score NaN
-  const int ps = min(p0 + (tid & 255), last);
+  const uint32_t ps = min((uint32_t)p0 + ((uint32_t)tid & 255u), last);
   const bool bad = e.scale < 0 || e.scale >= num_blocks;
-  const uint32_t v = *reinterpret_cast<const uint32_t*>(cache + (int64_t)(bad ? 0 : e.scale) * (BS * 132) +
-                                                        BS * 128 + (ps % BS) * 4);
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(cache + (uint64_t)(bad ? 0u : (uint32_t)e.scale) * (BS * 132) +
+                                                        (BS * 128u + (ps % BS) * 4u));
   sh.scale = bad ? 0x7FC00000u : v;
   return sh;
 }
@@ -118,15 +122,21 @@ __device__ __forceinline__ float read_scale(const uint8_t* stage, int g, int lan
   return reinterpret_cast<const float*>(stage + kScaleOff)[16 * g + (lane & 15)];
 }
 
-// Epilogue of one 16-key group: the row's score for key 16g + lane%16 (in every
-// 16-lane row of the wave).
-__device__ __forceinline__ float group_score(const f32x4_t (&acc)[4], const float (&wq)[4][4], float s) {
+// In-lane part of the epilogue of one 16-key group: the ReLU-weighted sum over the
+// 16 heads this lane holds, for key lane%16 of the group.
+__device__ __forceinline__ float group_part(const f32x4_t (&acc)[4], const float (&wq)[4][4]) {
   float part = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) part = fmaf(wq[mt][v], relu(acc[mt][v]), part);
-  return rows4_sum(part) * s + 0.0f;  // +0.0f: a zero score is +0
+  return part;
+}
+
+// Epilogue of one 16-key group for the per-wave direct path: the row's score for key
+// 16g + lane%16 (in every 16-lane row of the wave).
+__device__ __forceinline__ float group_score(const f32x4_t (&acc)[4], const float (&wq)[4][4], float s) {
+  return rows4_sum(group_part(acc, wq)) * s + 0.0f;  // +0.0f: a zero score is +0
 }
 
 template <int BS>
@@ -220,21 +230,22 @@ __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
           for (int p = p0 + lane; p < min(p0 + kStageKeys, k1); p += 64) __builtin_nontemporal_store(-INFINITY, out + p);
         return;
       }
-      float val = 0.0f;
+      float part[4];
 #pragma unroll
       for (int g = 0; g < kStageGroups; ++g) {
         const i32x8_t b = read_b(st, g, lane);
-        const float sg = read_scale(st, g, lane);
         f32x4_t acc[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-        const float sc = group_score(acc, wq, sg);
-        if ((lane >> 4) == (g & 3)) val = sc;
-        if ((g & 3) == 3) {  // 64 keys done: one coalesced store
-          const int p = p0 + 16 * (g - 3) + lane;
-          const float v = p >= n ? -INFINITY : val;
+        part[g & 3] = group_part(acc, wq);
+        if ((g & 3) == 3) {  // 64 keys done: lane l gets key l of the span, one store
+          const int sp = g >> 2;
+          const float sk = reinterpret_cast<const float*>(st + kScaleOff)[64 * sp + lane];
+          const float v0 = rows4_reduce_scatter(part[0], part[1], part[2], part[3]) * sk + 0.0f;
+          const int p = p0 + 64 * sp + lane;
+          const float v = p >= n ? -INFINITY : v0;  // (+0.0f above: a zero score is +0)
           if (p < k1 && (p < n || write_pad)) __builtin_nontemporal_store(v, out + p);
         }
       }
