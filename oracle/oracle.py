@@ -29,6 +29,9 @@ tests/test_oracle_*.py):
   hadamard_matrix, rmsnorm, rope,
   store_chain ............................. pinned (closed forms, invariants,
                                              scipy.linalg.hadamard)
+  q_prep .................................... pinned (per-vector brute force, the
+                                             rotation identities, RoPE's relative-
+                                             position property)
   score, score_rows ....................... pinned (exact-rational brute force,
                                              closed forms, invariants)
   topk ..................................... pinned (subset brute force, numpy and
@@ -226,6 +229,25 @@ def store_chain(x_bits: np.ndarray, positions: np.ndarray, flags: int, eps: floa
         h = hadamard_matrix(y.shape[-1]).astype(np.float64)
         y = (y @ h.T) / np.sqrt(float(y.shape[-1]))
     return y
+
+
+def q_prep(q_bits: np.ndarray, positions: np.ndarray, flags: int, base: float, rope_dim: int,
+           eps: float = 1e-6) -> np.ndarray:
+    """float64 query preparation: every (row, head) vector of the decoded bf16 query
+    [rows, heads, 128] goes through the same chain as an index key (optional
+    RMSNorm, interleaved RoPE on the trailing rope_dim at its row's position, the
+    normalised Hadamard rotation), all heads of a row sharing the row's position.
+
+    [ATOM-1507] "Where": the index query is prepared by interleaved RoPE on the
+    trailing rope_dim followed by a Hadamard rotation (plus fp8 quantisation, which
+    is quant_fp8 applied to these rows).  "Root cause found": the key must carry the
+    same rotation, since (H q).(H k) = q.k for the orthogonal H while (H q).k is a
+    scrambled product.  Returns float64 [rows, heads, 128]."""
+    q_bits = np.asarray(q_bits)
+    rows, heads, d = q_bits.shape
+    pos = np.repeat(np.asarray(positions, dtype=np.int64).reshape(rows), heads)
+    y = store_chain(q_bits.reshape(rows * heads, d), pos, flags, eps, base, rope_dim)
+    return y.reshape(rows, heads, d)
 
 
 # ----------------------------------------------------------------------------------
