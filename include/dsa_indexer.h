@@ -135,6 +135,34 @@ int32_t index_k_store(const void* x_bf16, int64_t n, const int32_t* positions,
                       void* hip_stream);
 
 /*
+ * indexer_q_prep - prepare index queries with the index key's chain.
+ * [ATOM-1507] "Where": the index query goes through interleaved RoPE on the trailing
+ * rope_dim, then a Hadamard rotation, then fp8 quantisation; "Root cause found":
+ * the key must carry the same rotation, because (H q).(H k) = q.k for the
+ * orthogonal H while (H q).k is a scrambled product ("Recommended fix" (A) drops
+ * the query's rotation instead: call this without IDX_STORE_HADAMARD).
+ * Every (row, head) vector goes through the steps of index_k_store selected by
+ * flags (RMSNorm, RoPE, Hadamard, same definitions), all heads of row r at
+ * position positions[r]; then
+ *   out_bf16          y rounded to bf16 (nearest even), and/or
+ *   codes / scales    the per-vector fp8 quantisation of indexer_quant_fp8.
+ * Arguments:
+ *   q_bf16        device bf16 [n_vec][128] = [rows][heads][128], row-major.
+ *   n_vec         rows * heads (0 is a no-op); must be a multiple of heads, with
+ *                 rows * ceil(heads / 4) <= 4 * INT32_MAX.
+ *   positions     device int32 [rows] (read only with IDX_STORE_ROPE).
+ *   out_bf16      NULL or device bf16 [n_vec][128].
+ *   codes, scales both NULL, or device uint8 [n_vec][128] and fp32 [n_vec].
+ *   prequant_dbg  NULL or device fp32 [n_vec][128]: y before rounding/quantisation.
+ * At least one output must be requested.  Errors: IDX_EINVAL for a bad size, flag,
+ * rope parameter, missing pointer or misaligned pointer (q_bf16, out_bf16, scales
+ * 4-byte; codes 2-byte; prequant_dbg 8-byte).
+ */
+int32_t indexer_q_prep(const void* q_bf16, int64_t n_vec, int32_t heads, const int32_t* positions,
+                       uint32_t flags, float rms_eps, float rope_base, int32_t rope_dim, void* out_bf16,
+                       uint8_t* codes, float* scales, float* prequant_dbg, void* hip_stream);
+
+/*
  * indexer_quant_fp8 - per-vector absmax fp8 quantisation of contiguous vectors of
  * 128 values (the query-side fp8 step of the pages' rope_rotate_activation,
  * [ATOM-1507] "Where"), with exactly the same rule as the fp8 store.

@@ -20,7 +20,7 @@ IDX_STORE_ALL = 7
 IDX_OP_TOPK, IDX_OP_SCORE_TOPK = 1, 2
 HEAD_DIM = 128
 
-EXPORTED = ("index_k_store", "indexer_quant_fp8", "indexer_score", "indexer_topk",
+EXPORTED = ("index_k_store", "indexer_q_prep", "indexer_quant_fp8", "indexer_score", "indexer_topk",
             "indexer_score_topk", "indexer_workspace_bytes", "indexer_last_error",
             "indexer_abi_version")
 
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH):
                                   ctypes.c_float, ctypes.c_size_t)
     sig = {
         "index_k_store": (i32, [vp, i64, vp, vp, KCache, u32, f32, f32, i32, vp, vp]),
+        "indexer_q_prep": (i32, [vp, i64, i32, vp, u32, f32, f32, i32, vp, vp, vp, vp, vp]),
         "indexer_quant_fp8": (i32, [vp, i64, vp, vp, vp]),
         "indexer_score": (i32, [vp, i32, vp, vp, i32, KCache, Rows, vp, i64, vp]),
         "indexer_topk": (i32, [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]),
@@ -150,6 +151,32 @@ def index_k_store(x, positions, slot_mapping, cache: KCache, flags: int = 0, rms
     _check("index_k_store", load_library().index_k_store(
         _ptr(x), n, _ptr(positions), _ptr(slot_mapping), cache, flags, rms_eps, rope_base, rope_dim,
         _ptr(prequant_dbg), _stream(stream)))
+
+
+def indexer_q_prep(q, positions, flags: int, rope_base: float = 10000.0, rope_dim: int = 64,
+                   out_bf16=None, codes=None, scales=None, rms_eps: float = 1e-6, prequant_dbg=None,
+                   stream=None):
+    """q: bf16 [rows, heads, 128]; positions: int32 [rows] (needed with IDX_STORE_ROPE)."""
+    import torch
+    _need(q, torch.bfloat16, "q")
+    _need(positions, torch.int32, "positions")
+    _need(out_bf16, torch.bfloat16, "out_bf16")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float32, "scales")
+    _need(prequant_dbg, torch.float32, "prequant_dbg")
+    if q.dim() != 3 or q.shape[-1] != HEAD_DIM:
+        raise ValueError("q must be [rows, heads, 128]")
+    rows, heads = q.shape[0], q.shape[1]
+    n_vec = rows * heads
+    for t, n, want in ((out_bf16, "out_bf16", n_vec * HEAD_DIM), (codes, "codes", n_vec * HEAD_DIM),
+                       (scales, "scales", n_vec), (prequant_dbg, "prequant_dbg", n_vec * HEAD_DIM)):
+        if t is not None and t.numel() != want:
+            raise ValueError(f"{n} must hold {want} elements")
+    if positions is not None and positions.numel() != rows:
+        raise ValueError("positions must hold one entry per row")
+    _check("indexer_q_prep", load_library().indexer_q_prep(
+        _ptr(q), n_vec, heads, _ptr(positions), flags, rms_eps, rope_base, rope_dim, _ptr(out_bf16),
+        _ptr(codes), _ptr(scales), _ptr(prequant_dbg), _stream(stream)))
 
 
 def indexer_quant_fp8(x, codes, scales, stream=None):

@@ -142,6 +142,42 @@ IDX_API int32_t index_k_store(const void* x_bf16, int64_t n, const int32_t* posi
                   "index_k_store");
 }
 
+IDX_API int32_t indexer_q_prep(const void* q_bf16, int64_t n_vec, int32_t heads, const int32_t* positions,
+                               uint32_t flags, float rms_eps, float rope_base, int32_t rope_dim,
+                               void* out_bf16, uint8_t* codes, float* scales, float* prequant_dbg,
+                               void* hip_stream) {
+  g_err.clear();
+  if (n_vec < 0) return fail(IDX_EINVAL, "n_vec must be >= 0");
+  if (heads < 1) return fail(IDX_EINVAL, "heads must be >= 1");
+  if (n_vec % heads) return fail(IDX_EINVAL, "n_vec %lld is not a multiple of heads %d", (long long)n_vec, heads);
+  if (flags & ~7u) return fail(IDX_EINVAL, "unknown flag bits 0x%x", flags & ~7u);
+  if (flags & IDX_STORE_ROPE) {
+    if (rope_dim < 2 || rope_dim > IDX_HEAD_DIM || (rope_dim & 1))
+      return fail(IDX_EINVAL, "rope_dim %d must be even and in [2, 128]", rope_dim);
+    if (!(rope_base > 0.0f) || !std::isfinite(rope_base)) return fail(IDX_EINVAL, "rope_base must be finite and > 0");
+  }
+  if ((flags & IDX_STORE_RMSNORM) && (!(rms_eps >= 0.0f) || !std::isfinite(rms_eps)))
+    return fail(IDX_EINVAL, "rms_eps must be finite and >= 0");
+  if ((codes == nullptr) != (scales == nullptr)) return fail(IDX_EINVAL, "codes and scales go together");
+  if (!out_bf16 && !codes && !prequant_dbg) return fail(IDX_EINVAL, "no output requested");
+  if (n_vec == 0) return IDX_OK;
+  if (n_vec > ((int64_t)1 << 40)) return fail(IDX_EINVAL, "n_vec too large");
+  if ((n_vec / heads) * (((int64_t)heads + 3) / 4) > (int64_t)INT32_MAX * 4)
+    return fail(IDX_EINVAL, "too many vectors for one launch (rows * ceil(heads / 4) > 4 * INT32_MAX)");
+  if (!q_bf16) return fail(IDX_EINVAL, "q_bf16 must be non-NULL");
+  if (!aligned(q_bf16, 4)) return fail(IDX_EINVAL, "q_bf16 must be 4-byte aligned");
+  if ((flags & IDX_STORE_ROPE) && !positions) return fail(IDX_EINVAL, "positions is required with IDX_STORE_ROPE");
+  if (positions && !aligned(positions, 4)) return fail(IDX_EINVAL, "positions must be 4-byte aligned");
+  if (out_bf16 && !aligned(out_bf16, 4)) return fail(IDX_EINVAL, "out_bf16 must be 4-byte aligned");
+  if (codes && !aligned(codes, 2)) return fail(IDX_EINVAL, "codes must be 2-byte aligned");
+  if (scales && !aligned(scales, 4)) return fail(IDX_EINVAL, "scales must be 4-byte aligned");
+  if (prequant_dbg && !aligned(prequant_dbg, 8)) return fail(IDX_EINVAL, "prequant_dbg must be 8-byte aligned");
+  return launched(dsa::launch_q_prep(static_cast<const uint16_t*>(q_bf16), n_vec, heads, positions, flags,
+                                     rms_eps, rope_base, rope_dim, static_cast<uint16_t*>(out_bf16), codes,
+                                     scales, prequant_dbg, static_cast<hipStream_t>(hip_stream)),
+                  "indexer_q_prep");
+}
+
 IDX_API int32_t indexer_quant_fp8(const void* x_bf16, int64_t n_vec, uint8_t* codes, float* scales,
                           void* hip_stream) {
   g_err.clear();

@@ -29,6 +29,10 @@ hipError_t launch_store(const uint16_t* x, int64_t n, const int32_t* pos, const 
                         const KCache& c, uint32_t flags, float eps, float rope_base, int rope_dim,
                         float* dbg, hipStream_t s);
 
+// query preparation: chain flags as for the store, all heads of a row at pos[row]
+hipError_t launch_q_prep(const uint16_t* x, int64_t n_vec, int heads, const int32_t* pos, uint32_t flags,
+                         float eps, float rope_base, int rope_dim, uint16_t* out_bf16, uint8_t* codes,
+                         float* scales, float* dbg, hipStream_t s);
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n_vec, uint8_t* codes, float* scales,
                             hipStream_t s);
 

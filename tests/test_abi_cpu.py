@@ -70,6 +70,37 @@ def test_store_validation():
     assert err(lib) == ""
 
 
+def test_q_prep_validation():
+    lib = dsa.load_library()
+    f = lib.indexer_q_prep
+    R, H = dsa.IDX_STORE_ROPE, dsa.IDX_STORE_HADAMARD
+    ok = (FAKE, 8, 4, FAKE, R | H, 1e-6, 1e4, 64, FAKE, None, None, None, None)
+    def call(**kw):
+        names = ("q", "n", "heads", "pos", "flags", "eps", "base", "rope_dim", "out", "codes", "scales", "dbg", "s")
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return f(*[a[n] for n in names])
+    assert call(n=-1) == dsa.IDX_EINVAL
+    assert call(heads=0) == dsa.IDX_EINVAL
+    assert call(n=7) == dsa.IDX_EINVAL and "multiple" in err(lib)
+    assert call(flags=8) == dsa.IDX_EINVAL and "flag" in err(lib)
+    assert call(rope_dim=63) == dsa.IDX_EINVAL and "rope_dim" in err(lib)
+    assert call(base=0.0) == dsa.IDX_EINVAL
+    assert call(flags=dsa.IDX_STORE_RMSNORM, eps=-1.0) == dsa.IDX_EINVAL
+    assert call(codes=FAKE) == dsa.IDX_EINVAL and "together" in err(lib)
+    assert call(out=None) == dsa.IDX_EINVAL and "output" in err(lib)
+    assert call(q=None) == dsa.IDX_EINVAL
+    assert call(q=FAKE + 2) == dsa.IDX_EINVAL and "aligned" in err(lib)
+    assert call(pos=None) == dsa.IDX_EINVAL and "positions" in err(lib)
+    assert call(out=FAKE + 2) == dsa.IDX_EINVAL
+    assert call(out=None, codes=FAKE + 1, scales=FAKE) == dsa.IDX_EINVAL
+    assert call(out=None, codes=FAKE, scales=FAKE + 2) == dsa.IDX_EINVAL
+    assert call(dbg=FAKE + 4) == dsa.IDX_EINVAL
+    # no RoPE: positions may be NULL; n = 0 is a no-op that never touches the GPU
+    assert call(n=0, q=None, pos=None, flags=H) == dsa.IDX_OK
+    assert err(lib) == ""
+
+
 def test_quant_validation():
     lib = dsa.load_library()
     f = lib.indexer_quant_fp8

@@ -54,6 +54,53 @@ def test_quant_fp8_bit_exact():
     assert bad.size == 0, (bad[:5], gc[tuple(bad[0])], oc[tuple(bad[0])])
 
 
+def near_tie_vectors():
+    """bf16 vectors whose quotients x / s land within 4 fp32 ulps of an e4m3 rounding
+    tie (or on it), found by search: for every bf16 amax in [2^-4, 2^10) and every
+    tie M between consecutive e4m3 magnitudes, y = bf16(M * s) with s = fl32(amax/448)
+    is kept when fl32(y / s) is that close to M.  Each vector holds amax (so the scale
+    is s), the hits for that amax with both signs, and zeros."""
+    amax = O.bf16_bits_to_f32(np.arange(0x3D80, 0x4480, dtype=np.uint16))
+    s = (amax / np.float32(448)).astype(np.float32)
+    mags = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    ties = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    ties = np.append(ties, np.float32(464))
+    y = O.bf16_bits_to_f32(gen.f32_to_bf16_bits((ties[None, :] * s[:, None]).astype(np.float32)))
+    q = (y / s[:, None]).astype(np.float32)
+    dist = np.abs(q.view(np.int32).astype(np.int64) - ties.view(np.int32)[None, :].astype(np.int64))
+    hit = (dist <= 4) & (y > 0) & (y <= amax[:, None])
+    rows = []
+    for i in np.flatnonzero(hit.any(axis=1)):
+        v = np.zeros(128, np.float32)
+        hv = y[i][hit[i]][:63]
+        v[0] = amax[i]
+        v[1:1 + hv.size] = hv
+        v[64:64 + hv.size] = -hv
+        rows.append(v)
+    return gen.f32_to_bf16_bits(np.stack(rows)), int(hit.sum()), int((dist[hit] == 0).sum())
+
+
+@pytest.mark.parametrize("entry", ["quant_fp8", "q_prep"])
+def test_quantisers_at_e4m3_ties(entry):
+    # the quantisers take the codes of y * (1/s) unless that product is near a tie;
+    # here every element is near one, and the codes must still be e4m3(RN32(y / s))
+    bits, n_hits, n_exact = near_tie_vectors()
+    assert n_hits > 1000 and n_exact > 0
+    x = bf16_tensor(bits)
+    codes = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(x.shape[0], dtype=torch.float32, device="cuda")
+    note(f"{entry} near-tie vectors n_vec={x.shape[0]} hits={n_hits}")
+    if entry == "quant_fp8":
+        dsa.indexer_quant_fp8(x, codes, scales)
+    else:
+        dsa.indexer_q_prep(x.view(-1, 1, 128), None, 0, codes=codes.view(-1, 1, 128), scales=scales.view(-1, 1))
+    torch.cuda.synchronize()
+    oc, os_ = O.quant_fp8(O.bf16_bits_to_f32(bits))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    bad = np.argwhere(codes.cpu().numpy() != oc)
+    assert bad.size == 0, bad[:5]
+
+
 def test_quant_fp8_ragged_and_empty():
     rng = np.random.default_rng(1)
     for n in (1, 15, 17, 1000):
