@@ -57,7 +57,8 @@ def source_hash(files):
 
 
 KERNEL_SOURCES = {"score_decode": ["score_decode.hip", "common.hpp"],
-                  "score_prefill": ["score_prefill.hip", "common.hpp"]}
+                  "score_prefill": ["score_prefill.hip", "common.hpp"],
+                  "q_prep": ["store.hip", "common.hpp"]}
 
 
 def traffic_from_profile(kernel: str, workload: str):
@@ -160,6 +161,57 @@ class Runner:
                 "kernel": "score_decode"}
 
 
+def bench_q_prep(args, run):
+    """Time indexer_q_prep on the workload's query tensor [rows][64][128]: interleaved
+    RoPE on the trailing 64 dims at each row's position, the Hadamard rotation and
+    fp8 quantisation (codes + per-vector scale), the query side of the path.  One
+    launch per step; HIP events on the launch stream bracket the timed steps."""
+    torch, dsa, wl = run.torch, run.dsa, run.wl
+    rows, heads = wl.q_bits.shape[0], wl.q_bits.shape[1]
+    pos = torch.from_numpy((np.asarray(wl.row_len, np.int64) - 1).astype(np.int32)).cuda()
+    codes = torch.empty(run.q.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, heads), dtype=torch.float32, device="cuda")
+    flags = dsa.IDX_STORE_ROPE | dsa.IDX_STORE_HADAMARD
+
+    def launch():
+        dsa.indexer_q_prep(run.q, pos, flags, wl.rope_base, wl.rope_dim, codes=codes, scales=scales)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        launch()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    n_vec = rows * heads
+    nbytes = n_vec * (256 + 128 + 4) + rows * 4      # q in, codes + scale out, positions
+    achieved = nbytes / (ms / 1e3) / 1e9
+    return {
+        "metric": "query vectors prepared/s (RoPE + Hadamard + fp8) at 1 GPU",
+        "value": n_vec / (ms / 1e3),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload} queries", "rows": rows, "heads": heads, "head_dim": 128,
+                   "rope_dim": wl.rope_dim, "rope_base": wl.rope_base, "flags": "rope|hadamard",
+                   "output": "fp8 e4m3 codes + fp32 scale", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "q_prep", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile("q_prep", args.workload),
+                     "algorithmic_per_launch": nbytes},
+    }
+
+
 def cpu_baseline(wl, kd, budget_s=15.0, min_s=10.0):
     """The oracle (numpy float64, BLAS threads as configured) on a bounded sample of
     the same workload: whole rows (store chain of the row's new tokens, key
@@ -230,6 +282,9 @@ def main():
                     help="record the per-kernel timing events on every N-th timed step (each record is a "
                          "host call; on the short decode steps recording them every step would leave the "
                          "GPU waiting on the host)")
+    ap.add_argument("--op", default="step", choices=["step", "q_prep"],
+                    help="step: the indexer step (default); q_prep: the query preparation alone, on "
+                         "the workload's queries")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -257,6 +312,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(f"[bench] copy calibration: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
+
+    if args.op == "q_prep":
+        print(json.dumps(bench_q_prep(args, run)), flush=True)
+        return
 
     for i in range(args.warmup):
         run.step(i)

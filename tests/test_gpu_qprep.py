@@ -118,3 +118,37 @@ def test_rotated_query_and_key_score_as_the_unrotated_pair():
     # and the plain, unrotated pair agrees within the bf16 rounding of the operands
     plain = oracle_scores(wl, OracleKeys(wl, "bf16"))
     check_scores(got, plain, wl.row_len, 8 * RTOL["bf16"])
+
+
+@pytest.mark.parametrize("S", [4500, 22000])
+def test_asymmetric_rotation_loses_the_needle_on_gpu(S):
+    # the pages' root cause on the GPU path end to end: queries prepared with the
+    # Hadamard, a needle of typical key norm aligned with sum_h w_h q_h, scored and
+    # selected by the fused score + top-512.  Keys stored with the same rotation keep
+    # the needle (rank 1 in the oracle); keys stored without it drop it (oracle rank
+    # 3544 at S=4500 and 15418 at S=22000, far outside the top 512).
+    k = 512
+    wl = gen.make([S], key_dtype="bf16", k=k, seed=0, needle_depth=None)
+    keys = O.bf16_bits_to_f64(wl.keys_bits[0])[:S]
+    q = O.bf16_bits_to_f64(wl.q_bits[0])
+    v = (wl.w[0].astype(np.float64)[:, None] * q).sum(0)
+    p = S // 2
+    typical = np.median(np.linalg.norm(keys, axis=1))
+    wl.keys_bits[0][p] = gen.f32_to_bf16_bits((typical * v / np.linalg.norm(v)).astype(np.float32))
+    g = GpuWorkload(wl, key_dtype="bf16")
+    qr = torch.empty_like(g.q)
+    note(f"asymmetric-rotation needle S={S}")
+    dsa.indexer_q_prep(g.q, None, H, out_bf16=qr)
+
+    def selected(flags):
+        buf = torch.full_like(g.buf, 0xFF)
+        cache = dsa.kcache(buf, dsa.IDX_BF16, wl.block_size, wl.num_blocks)
+        dsa.index_k_store(g.prefix_x, None, g.prefix_slots, cache, flags)
+        ws = dsa.alloc_workspace(dsa.IDX_OP_SCORE_TOPK, wl.rows, wl.max_row_len, k)
+        out = torch.empty((wl.rows, k), dtype=torch.int32, device="cuda")
+        dsa.indexer_score_topk(qr, g.w, cache, g.rows, k, out, ws)
+        torch.cuda.synchronize()
+        return set(out[0].cpu().numpy().tolist())
+
+    assert p in selected(H)
+    assert p not in selected(0)
