@@ -36,6 +36,10 @@ tests/test_oracle_*.py):
                                              closed forms, invariants)
   topk ..................................... pinned (subset brute force, numpy and
                                              torch library routines)
+  translate ................................ pinned (hand-worked example, the
+                                             identity table's closed form, the
+                                             store's slot of every stored position,
+                                             injectivity on a shuffled table)
   jaccard .................................. pinned (the printed table of the
                                              synthetic fp8-vs-bf16 test)
 """
@@ -343,6 +347,50 @@ def rank_of(scores_row: np.ndarray, n: int, p: int) -> int:
     """1-based rank of position p under (score desc, position asc)."""
     s = np.asarray(scores_row[:n], dtype=np.float64)
     return int(np.sum(s > s[p]) + np.sum(s[:p] == s[p]) + 1)
+
+
+# ----------------------------------------------------------------------------------
+# Logical -> physical translation of the selections
+# ----------------------------------------------------------------------------------
+
+
+def translate(idx, block_table, row_seq, row_len, block_size: int, num_blocks: int,
+              max_row_len: int | None = None) -> np.ndarray:
+    """Physical cache slot of every selected logical key position.
+
+    The pages name the step (csa_translate_pack, logical -> physical) and say it is
+    correct for arbitrary index lists ([ATOM-1507] "How it was isolated"); they do
+    not print it.  READING: the paged layout the store writes, where position t of
+    sequence s sits in logical block t // bs at offset t % bs, and the block table
+    names the physical block b of that logical block:
+        slot = b * bs + t % bs.
+    An entry that addresses no visible key maps to -1: the -1 padding of a short
+    row, t outside 0 <= t < min(row_len[r], max_row_len), a row whose sequence id is
+    outside the table, a logical block past the table's width, or a physical block
+    id outside [0, num_blocks).
+
+    idx [rows][k] int; block_table [num_seqs][max_blocks]; row_seq, row_len [rows].
+    Returns int64 [rows][k].
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    table = np.asarray(block_table, dtype=np.int64)
+    num_seqs, max_blocks = table.shape
+    rows, k = idx.shape
+    out = np.full((rows, k), -1, dtype=np.int64)
+    for r in range(rows):
+        s = int(row_seq[r])
+        n = max(int(row_len[r]), 0)
+        if max_row_len is not None:
+            n = min(n, int(max_row_len))
+        if not 0 <= s < num_seqs:
+            continue
+        t = idx[r]
+        lb = np.where(t >= 0, t // block_size, 0)
+        ok = (t >= 0) & (t < n) & (lb < max_blocks)
+        b = np.where(ok, table[s, np.minimum(lb, max_blocks - 1)], -1)
+        ok &= (b >= 0) & (b < num_blocks)
+        out[r] = np.where(ok, b * block_size + t % block_size, -1)
+    return out
 
 
 # ----------------------------------------------------------------------------------
