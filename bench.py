@@ -58,7 +58,8 @@ def source_hash(files):
 
 KERNEL_SOURCES = {"score_decode": ["score_decode.hip", "common.hpp"],
                   "score_prefill": ["score_prefill.hip", "common.hpp"],
-                  "q_prep": ["store.hip", "common.hpp"]}
+                  "q_prep": ["store.hip", "common.hpp"],
+                  "translate": ["topk.hip", "common.hpp"]}
 
 
 def traffic_from_profile(kernel: str, workload: str):
@@ -212,6 +213,77 @@ def bench_q_prep(args, run):
     }
 
 
+def bench_translate(args, run):
+    """Time indexer_translate on selections shaped like the step's top-k output
+    (k sorted distinct visible positions per row, -1 padding on short rows), and the
+    cost the fused slots add to indexer_score_topk (same call with and without
+    out_slots, on the same stream, alternating)."""
+    torch, dsa, wl = run.torch, run.dsa, run.wl
+    rng = np.random.default_rng(0)
+    k = wl.k
+    sel = np.full((wl.rows, k), -1, np.int32)
+    for r in range(wl.rows):
+        n = int(wl.row_len[r])
+        m = min(n, k)
+        sel[r, :m] = np.sort(rng.choice(n, m, replace=False))
+    idx = torch.from_numpy(sel).cuda()
+    slots = torch.empty((wl.rows, k), dtype=torch.int64, device="cuda")
+    cache = run.caches[0]
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms = timed(lambda: dsa.indexer_translate(idx, cache, run.rows, slots), args.steps)
+    # fused: the whole score + top-k with and without the slots output
+    q, qs = (run.q_codes, run.q_scale) if run.prefill else (run.q, None)
+    if run.prefill:
+        dsa.indexer_quant_fp8(run.q, run.q_codes, run.q_scale)
+    ws = dsa.alloc_workspace(dsa.IDX_OP_SCORE_TOPK, wl.rows, wl.max_row_len, k)
+    out = torch.empty((wl.rows, k), dtype=torch.int32, device="cuda")
+    fsteps = max(3, min(args.steps, 50))
+    plain, fused = [], []
+    for _ in range(3):
+        plain.append(timed(lambda: dsa.indexer_score_topk(q, run.w, cache, run.rows, k, out, ws, q_scale=qs), fsteps))
+        fused.append(timed(lambda: dsa.indexer_score_topk(q, run.w, cache, run.rows, k, out, ws, q_scale=qs,
+                                                          out_slots=slots), fsteps))
+    n = wl.rows * k
+    table_bytes = int(wl.block_table.size) * 4
+    nbytes = n * (4 + 8) + table_bytes + wl.rows * 8
+    achieved = nbytes / (ms / 1e3) / 1e9
+    return {
+        "metric": "selected indices translated to physical slots/s at 1 GPU",
+        "value": n / (ms / 1e3),
+        "unit": "indices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int64",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload} selections", "rows": wl.rows, "k": k,
+                   "block_size": wl.block_size, "parallelism": "single GPU"},
+        "fused_in_score_topk": {"ms_without_slots": float(np.median(plain)),
+                                "ms_with_slots": float(np.median(fused)),
+                                "added_ms": float(np.median(fused) - np.median(plain))},
+        "roofline": {"bound": "hbm", "kernel": "translate", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile("translate", args.workload),
+                     "algorithmic_per_launch": nbytes},
+    }
+
+
 def cpu_baseline(wl, kd, budget_s=15.0, min_s=10.0):
     """The oracle (numpy float64, BLAS threads as configured) on a bounded sample of
     the same workload: whole rows (store chain of the row's new tokens, key
@@ -282,9 +354,10 @@ def main():
                     help="record the per-kernel timing events on every N-th timed step (each record is a "
                          "host call; on the short decode steps recording them every step would leave the "
                          "GPU waiting on the host)")
-    ap.add_argument("--op", default="step", choices=["step", "q_prep"],
+    ap.add_argument("--op", default="step", choices=["step", "q_prep", "translate"],
                     help="step: the indexer step (default); q_prep: the query preparation alone, on "
-                         "the workload's queries")
+                         "the workload's queries; translate: logical -> physical translation of "
+                         "top-k-shaped selections, and what the fused slots add to score + top-k")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -315,6 +388,9 @@ def main():
 
     if args.op == "q_prep":
         print(json.dumps(bench_q_prep(args, run)), flush=True)
+        return
+    if args.op == "translate":
+        print(json.dumps(bench_translate(args, run)), flush=True)
         return
 
     for i in range(args.warmup):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define IDX_ABI_VERSION 1
+#define IDX_ABI_VERSION 2
 #define IDX_HEAD_DIM 128
 
 typedef enum {
@@ -219,6 +219,9 @@ int32_t indexer_topk(const float* scores, int64_t ld, const int32_t* row_len, in
  * fix" and "How it was isolated").  Same arguments as the two calls; the scores
  * live in the workspace.
  *   out_idx     device int32 [rows][k] (as indexer_topk).
+ *   out_slots   NULL, or device int64 [rows][k]: the physical cache slot of each
+ *               selected position, as indexer_translate maps it, written by the
+ *               top-k's last pass (-1 for padding).
  *   out_scores  NULL, or device fp32 [rows][k]: the score of each selected
  *               position, -inf for padding.
  *   ws          at least indexer_workspace_bytes(IDX_OP_SCORE_TOPK, rows,
@@ -226,8 +229,25 @@ int32_t indexer_topk(const float* scores, int64_t ld, const int32_t* row_len, in
  */
 int32_t indexer_score_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
                            int32_t heads, idx_kcache cache, idx_rows rows, int32_t k,
-                           int32_t* out_idx, float* out_scores, void* ws, size_t ws_bytes,
-                           void* hip_stream);
+                           int32_t* out_idx, int64_t* out_slots, float* out_scores, void* ws,
+                           size_t ws_bytes, void* hip_stream);
+
+/*
+ * indexer_translate - selected logical key positions -> physical cache slots (the
+ * logical -> physical step after the top-k, which must be right for arbitrary index
+ * lists, [ATOM-1507] "How it was isolated").  For row r < rows.rows and j < k, with
+ * t = idx[r*ld_idx + j], s = rows.row_seq[r] and bs = cache.block_size:
+ *   slots[r*ld_slots + j] = b*bs + t%bs,  b = rows.block_table[s*max_blocks + t/bs],
+ * when 0 <= t < min(row_len[r], max_row_len), 0 <= s < num_seqs, t/bs < max_blocks
+ * and 0 <= b < cache.num_blocks; otherwise -1 (so -1 padding stays -1).
+ *   idx    device int32 [rows][ld_idx];  slots  device int64 [rows][ld_slots].
+ *   cache  only block_size and num_blocks are read (base may be NULL).
+ * Errors: IDX_EINVAL for k < 0, a stride below k, bad rows/cache geometry, missing
+ * or misaligned pointers (idx 4-byte, slots 8-byte); IDX_EUNSUPPORTED for a block
+ * size other than 32 or 64.  rows.rows == 0 or k == 0 is a no-op.
+ */
+int32_t indexer_translate(const int32_t* idx, int64_t ld_idx, int32_t k, idx_kcache cache,
+                          idx_rows rows, int64_t* slots, int64_t ld_slots, void* hip_stream);
 
 /* Workspace bytes needed by an op (IDX_OP_TOPK or IDX_OP_SCORE_TOPK); 0 on bad
  * arguments. */

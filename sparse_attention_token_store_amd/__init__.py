@@ -21,7 +21,7 @@ IDX_OP_TOPK, IDX_OP_SCORE_TOPK = 1, 2
 HEAD_DIM = 128
 
 EXPORTED = ("index_k_store", "indexer_q_prep", "indexer_quant_fp8", "indexer_score", "indexer_topk",
-            "indexer_score_topk", "indexer_workspace_bytes", "indexer_last_error",
+            "indexer_score_topk", "indexer_translate", "indexer_workspace_bytes", "indexer_last_error",
             "indexer_abi_version")
 
 
@@ -66,7 +66,8 @@ def load_library(path: str = LIB_PATH):
         "indexer_quant_fp8": (i32, [vp, i64, vp, vp, vp]),
         "indexer_score": (i32, [vp, i32, vp, vp, i32, KCache, Rows, vp, i64, vp]),
         "indexer_topk": (i32, [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]),
-        "indexer_score_topk": (i32, [vp, i32, vp, vp, i32, KCache, Rows, i32, vp, vp, vp, sz, vp]),
+        "indexer_score_topk": (i32, [vp, i32, vp, vp, i32, KCache, Rows, i32, vp, vp, vp, vp, sz, vp]),
+        "indexer_translate": (i32, [vp, i64, i32, KCache, Rows, vp, i64, vp]),
         "indexer_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "indexer_last_error": (ctypes.c_char_p, []),
         "indexer_abi_version": (i32, []),
@@ -227,15 +228,31 @@ def indexer_topk(scores, row_len, max_row_len: int, k: int, out_idx, ws=None, st
 
 
 def indexer_score_topk(q, w, cache: KCache, rows: Rows, k: int, out_idx, ws, out_scores=None,
-                       q_scale=None, stream=None):
+                       q_scale=None, out_slots=None, stream=None):
     import torch
     q_dtype, heads = _q_args(q, q_scale, w)
     _need(out_idx, torch.int32, "out_idx")
     _need(out_scores, torch.float32, "out_scores")
+    _need(out_slots, torch.int64, "out_slots")
+    if out_slots is not None and out_slots.numel() < out_idx.numel():
+        raise ValueError("out_slots must hold [rows, k] entries")
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("indexer_score_topk", load_library().indexer_score_topk(
         _ptr(q), q_dtype, _ptr(q_scale), _ptr(w), heads, cache, rows, k, _ptr(out_idx),
-        _ptr(out_scores), _ptr(ws), nbytes, _stream(stream)))
+        _ptr(out_slots), _ptr(out_scores), _ptr(ws), nbytes, _stream(stream)))
+
+
+def indexer_translate(idx, cache: KCache, rows: Rows, out_slots, stream=None):
+    """Physical cache slots of the index lists idx [rows, k] (int32) into out_slots
+    [rows, k] (int64); -1 wherever an entry addresses no visible key."""
+    import torch
+    _need(idx, torch.int32, "idx")
+    _need(out_slots, torch.int64, "out_slots")
+    if idx.dim() != 2 or tuple(out_slots.shape) != tuple(idx.shape) or idx.shape[0] != rows.rows:
+        raise ValueError("idx and out_slots must both be [rows, k]")
+    _check("indexer_translate", load_library().indexer_translate(
+        _ptr(idx), idx.shape[1], idx.shape[1], cache, rows, _ptr(out_slots), out_slots.shape[1],
+        _stream(stream)))
 
 
 def alloc_workspace(op: int, rows: int, max_row_len: int, k: int, device="cuda"):

@@ -82,6 +82,10 @@ dsa::KCache to_kc(const idx_kcache& c) {
 dsa::Rows to_rows(const idx_rows& r) {
   return dsa::Rows{r.block_table, r.max_blocks, r.num_seqs, r.row_seq, r.row_len, r.rows, r.max_row_len};
 }
+dsa::SlotMap to_map(const idx_kcache& c, const idx_rows& r, int64_t* slots, int64_t ld) {
+  return dsa::SlotMap{r.block_table, r.row_seq,   r.row_len,    r.max_blocks, r.num_seqs,
+                      c.block_size,  r.max_row_len, c.num_blocks, slots,        ld};
+}
 
 int32_t launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(IDX_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
@@ -240,17 +244,19 @@ IDX_API int32_t indexer_topk(const float* scores, int64_t ld, const int32_t* row
   if (need && (!ws || ws_bytes < need))
     return fail(IDX_EWORKSPACE, "workspace of %zu bytes required, %zu given", need, ws ? ws_bytes : (size_t)0);
   if (need && !aligned(ws, 256)) return fail(IDX_EINVAL, "ws must be 256-byte aligned");
-  return launched(dsa::launch_topk(scores, ld, row_len, rows, max_row_len, k, out_idx, nullptr, ws,
-                                   static_cast<hipStream_t>(hip_stream)),
+  return launched(dsa::launch_topk(scores, ld, row_len, rows, max_row_len, k, out_idx, nullptr,
+                                   dsa::SlotMap{}, ws, static_cast<hipStream_t>(hip_stream)),
                   "indexer_topk");
 }
 
 IDX_API int32_t indexer_score_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
                            int32_t heads, idx_kcache cache, idx_rows rows, int32_t k, int32_t* out_idx,
-                           float* out_scores, void* ws, size_t ws_bytes, void* hip_stream) {
+                           int64_t* out_slots, float* out_scores, void* ws, size_t ws_bytes,
+                           void* hip_stream) {
   g_err.clear();
   if (int32_t e = check_score_args(q, q_dtype, q_scale, w, heads, cache, rows)) return e;
   if (int32_t e = check_topk_common(rows.rows, rows.max_row_len, k, out_idx)) return e;
+  if (out_slots && !aligned(out_slots, 8)) return fail(IDX_EINVAL, "out_slots must be 8-byte aligned");
   if (out_scores && !aligned(out_scores, 4)) return fail(IDX_EINVAL, "out_scores must be 4-byte aligned");
   if (rows.rows == 0) return IDX_OK;
   const size_t need = score_bytes(rows.rows, rows.max_row_len) +
@@ -265,8 +271,29 @@ IDX_API int32_t indexer_score_topk(const void* q, int32_t q_dtype, const float* 
     if (int32_t e = launch_scores(q, q_dtype, q_scale, w, cache, rows, sc, ld, false, s)) return e;
   void* tws = static_cast<uint8_t*>(ws) + score_bytes(rows.rows, rows.max_row_len);
   return launched(dsa::launch_topk(sc, ld, rows.row_len, rows.rows, rows.max_row_len, k, out_idx,
-                                   out_scores, tws, s),
+                                   out_scores, to_map(cache, rows, out_slots, k), tws, s),
                   "indexer_score_topk");
+}
+
+IDX_API int32_t indexer_translate(const int32_t* idx, int64_t ld_idx, int32_t k, idx_kcache cache,
+                                  idx_rows rows, int64_t* slots, int64_t ld_slots, void* hip_stream) {
+  g_err.clear();
+  if (k < 0) return fail(IDX_EINVAL, "k must be >= 0");
+  if (ld_idx < k || ld_slots < k) return fail(IDX_EINVAL, "ld_idx and ld_slots must be >= k");
+  if (cache.block_size != 32 && cache.block_size != 64)
+    return fail(IDX_EUNSUPPORTED, "cache.block_size %d unsupported (32 or 64)", cache.block_size);
+  if (cache.num_blocks < 1 || cache.num_blocks > (int64_t)INT32_MAX)
+    return fail(IDX_EINVAL, "cache.num_blocks must be in [1, INT32_MAX]");
+  if (int32_t e = check_rows(rows)) return e;
+  if ((int64_t)rows.max_row_len > (int64_t)rows.max_blocks * cache.block_size)
+    return fail(IDX_EINVAL, "max_row_len %d exceeds max_blocks*block_size", rows.max_row_len);
+  if (rows.rows == 0 || k == 0) return IDX_OK;
+  if (!idx || !slots) return fail(IDX_EINVAL, "idx and slots must be non-NULL");
+  if (!aligned(idx, 4)) return fail(IDX_EINVAL, "idx must be 4-byte aligned");
+  if (!aligned(slots, 8)) return fail(IDX_EINVAL, "slots must be 8-byte aligned");
+  return launched(dsa::launch_translate(idx, ld_idx, rows.rows, k, to_map(cache, rows, slots, ld_slots),
+                                        static_cast<hipStream_t>(hip_stream)),
+                  "indexer_translate");
 }
 
 }  // extern "C"

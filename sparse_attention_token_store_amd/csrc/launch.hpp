@@ -46,10 +46,31 @@ hipError_t launch_score_prefill(const uint8_t* q, const float* q_scale, const fl
                                 const KCache& c, const Rows& r, float* scores, int64_t ld,
                                 bool write_pad, hipStream_t s);
 
-// top-k over fp32 score rows; ws of topk_ws_bytes(rows, max_row_len, k) bytes.
+// Logical key position -> physical cache slot of a row's selections: the row's
+// sequence, visible length and block table, the cache geometry, and where the slots
+// go (slots == nullptr: no translation).
+struct SlotMap {
+  const int32_t* block_table;
+  const int32_t* row_seq;
+  const int32_t* row_len;
+  int max_blocks;
+  int num_seqs;
+  int block_size;
+  int max_row_len;
+  int64_t num_blocks;
+  int64_t* slots;
+  int64_t ld;
+};
+
+// top-k over fp32 score rows; ws of topk_ws_bytes(rows, max_row_len, k) bytes.  The
+// last level also writes the physical slot of every selection when map.slots is set.
 size_t topk_ws_bytes(int rows, int max_row_len, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_len, int rows,
-                       int max_row_len, int k, int32_t* out_idx, float* out_scores, void* ws,
-                       hipStream_t s);
+                       int max_row_len, int k, int32_t* out_idx, float* out_scores,
+                       const SlotMap& map, void* ws, hipStream_t s);
+
+// physical slots of arbitrary index lists idx [rows][ld_idx] (first k of each row)
+hipError_t launch_translate(const int32_t* idx, int64_t ld_idx, int rows, int k, const SlotMap& map,
+                            hipStream_t s);
 
 }  // namespace dsa

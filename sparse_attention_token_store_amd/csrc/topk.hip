@@ -22,10 +22,14 @@
 //  4. Every key above tau is kept plus the first `rem` keys equal to it: with
 //     position-ordered counts G (greater) and E (equal) of the keys before a key,
 //     its output slot is G + min(E, rem).
+//  5. Optionally (a slot map is given) the last level translates its selections to
+//     physical cache slots in one pass after every emit.
 // Rows longer than one chunk are reduced level by level: each chunk keeps its own
 // top-k (exact: an element of the row's top-k under the order (score desc,
 // position asc) is also in its chunk's top-k), the survivors stay in position
 // order, and the next level selects among them.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -162,14 +166,29 @@ __device__ __forceinline__ void scan_table(uint32_t* tab, int E, uint32_t* total
   if (lane == 63) *total = incl;
 }
 
+// Physical cache slot of key position t of row r (the paged layout of the store:
+// logical block t / bs at offset t % bs, the block table naming the physical block),
+// or -1 when t is not a visible position of the row or a sequence or block id lies
+// outside its table.
+__device__ __forceinline__ int64_t physical_slot(const SlotMap& m, int64_t r, int32_t t) {
+  const int seq = m.row_seq[r];
+  const int len = min(max(m.row_len[r], 0), m.max_row_len);
+  if ((unsigned)seq >= (unsigned)m.num_seqs || t < 0 || t >= len) return -1;
+  const int lb = t / m.block_size;
+  if (lb >= m.max_blocks) return -1;
+  const int32_t b = m.block_table[(int64_t)seq * m.max_blocks + lb];
+  if (b < 0 || (int64_t)b >= m.num_blocks) return -1;
+  return (int64_t)b * m.block_size + (t - lb * m.block_size);
+}
+
 // kFirst: source is the score matrix; else a candidate list.  kLast: write the
-// final out_idx / out_scores; else the next candidate list.  vec: 16-byte loads of
+// final out_idx / out_scores (and the slots of map); else the next candidate list.  vec: 16-byte loads of
 // the source are aligned (score rows with ld % 4 == 0; lists always).
 template <int R, bool kFirst, bool kLast>
 __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     const float* __restrict__ scores, int64_t ld, Lists src, Lists dst,
     const int32_t* __restrict__ row_len, int max_row_len, int k, int nlevel, LevelChunks chunks,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_scores, int vec) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_scores, SlotMap map, int vec) {
   static_assert(R % 4 == 0, "slots come in groups of four");
   constexpr int G = R / 4;             // groups of four per thread
   constexpr int C = R * kThreads;      // chunk length
@@ -199,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     for (int p = nc + tid; p < k; p += kThreads) {
       out_idx[(int64_t)r * k + p] = -1;
       if (out_scores) out_scores[(int64_t)r * k + p] = -INFINITY;
+      if (map.slots) map.slots[(int64_t)r * map.ld + p] = -1;
     }
   }
   if (nc <= 0) return;
@@ -257,12 +277,27 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     }
   };
 
+  // 5. (last level, with a slot map) the physical slot of every selection: one pass
+  // over this row's out_idx after every emit, read back from L2 once the barrier has
+  // made the workgroup's writes visible, so each selection costs one table gather.
+  auto finish_slots = [&]() {
+    if constexpr (kLast) {
+      if (map.slots) {
+        __syncthreads();
+        const int m = min(nc, k);
+        for (int p = tid; p < m; p += kThreads)
+          map.slots[(int64_t)r * map.ld + p] = physical_slot(map, r, out_idx[(int64_t)r * k + p]);
+      }
+    }
+  };
+
   if (nc <= k) {  // everything survives, in order
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int li = li_of(j >> 2, j & 3);
       if (li < nc) emit(li, li, key[j]);
     }
+    finish_slots();
     return;
   }
 
@@ -467,17 +502,30 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
       }
     }
   }
+  finish_slots();
+}
+
+// Slots of arbitrary index lists: one thread per entry of the flattened [rows][k]
+// list, grid-strided.
+__global__ __launch_bounds__(256) void translate_kernel(const int32_t* __restrict__ idx, int64_t ld_idx,
+                                                        int64_t rows, int k, SlotMap map) {
+  const int64_t total = rows * k;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / k, j = e - r * k;
+    map.slots[r * map.ld + j] = physical_slot(map, r, idx[r * ld_idx + j]);
+  }
 }
 
 template <bool kFirst, bool kLast>
 hipError_t launch_level(int R, dim3 grid, hipStream_t s, const float* scores, int64_t ld,
                         Lists src, Lists dst, const int32_t* row_len, int max_row_len, int k,
-                        int nlevel, LevelChunks chunks, int32_t* out_idx, float* out_scores, int vec) {
+                        int nlevel, LevelChunks chunks, int32_t* out_idx, float* out_scores,
+                        const SlotMap& map, int vec) {
 #define DSA_TOPK_CASE(RR)                                                                      \
   case RR:                                                                                     \
     hipLaunchKernelGGL((topk_level_kernel<RR, kFirst, kLast>), grid, dim3(kThreads), 0, s,    \
                        scores, ld, src, dst, row_len, max_row_len, k, nlevel, chunks, out_idx, \
-                       out_scores, vec);                                                       \
+                       out_scores, map, vec);                                                  \
     break;
   switch (R) {
     DSA_TOPK_CASE(4)
@@ -548,8 +596,8 @@ size_t topk_ws_bytes(int rows, int max_row_len, int k) {
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_len, int rows,
-                       int max_row_len, int k, int32_t* out_idx, float* out_scores, void* ws,
-                       hipStream_t s) {
+                       int max_row_len, int k, int32_t* out_idx, float* out_scores,
+                       const SlotMap& map, void* ws, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const Plan p = make_plan(max_row_len, k);
   Lists none{nullptr, nullptr, 0};
@@ -560,7 +608,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_len, 
   if (p.levels == 1) {
     const int R = (int)(p.chunk[0] / kThreads);
     return launch_level<true, true>(R, dim3(1, rows), s, scores, ld, none, none, row_len,
-                                    max_row_len, k, 0, chunks, out_idx, out_scores, vec);
+                                    max_row_len, k, 0, chunks, out_idx, out_scores, map, vec);
   }
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   const int64_t cap = list_cap(p);
@@ -580,16 +628,26 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_len, 
     const Lists dst = last ? none : L[l & 1];
     if (first)
       e = launch_level<true, false>(R, dim3(nchunks, rows), s, scores, ld, src, dst, row_len,
-                                    max_row_len, k, 0, chunks, out_idx, out_scores, vec);
+                                    max_row_len, k, 0, chunks, out_idx, out_scores, map, vec);
     else if (!last)
       e = launch_level<false, false>(R, dim3(nchunks, rows), s, scores, ld, src, dst, row_len,
-                                     max_row_len, k, l, chunks, out_idx, out_scores, 1);
+                                     max_row_len, k, l, chunks, out_idx, out_scores, map, 1);
     else
       e = launch_level<false, true>(R, dim3(1, rows), s, scores, ld, src, dst, row_len,
-                                    max_row_len, k, l, chunks, out_idx, out_scores, 1);
+                                    max_row_len, k, l, chunks, out_idx, out_scores, map, 1);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_translate(const int32_t* idx, int64_t ld_idx, int rows, int k, const SlotMap& map,
+                            hipStream_t s) {
+  const int64_t total = (int64_t)rows * k;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 1 << 16);
+  hipLaunchKernelGGL(translate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, idx, ld_idx, (int64_t)rows, k,
+                     map);
+  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(dsa.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.indexer_abi_version() == 1
+    assert lib.indexer_abi_version() == 2
 
 
 FAKE = 1 << 20          # never dereferenced: every call below fails validation first
@@ -151,8 +151,11 @@ def test_topk_validation_and_workspace():
     st = lib.indexer_score_topk
     need2 = lib.indexer_workspace_bytes(dsa.IDX_OP_SCORE_TOPK, 4, 100, 8)
     assert need2 >= 4 * 128 * 4
-    assert st(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 8, FAKE, None, ALIGNED, need2 - 1, None) == dsa.IDX_EWORKSPACE
-    assert st(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 0, FAKE, None, ALIGNED, need2, None) == dsa.IDX_EINVAL
+    assert st(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 8, FAKE, None, None, ALIGNED, need2 - 1, None) == dsa.IDX_EWORKSPACE
+    assert st(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 0, FAKE, None, None, ALIGNED, need2, None) == dsa.IDX_EINVAL
+    # out_slots must be 8-byte aligned
+    assert st(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 8, FAKE, FAKE + 4, None, ALIGNED, need2, None) == dsa.IDX_EINVAL
+    assert "out_slots" in err(lib)
     assert lib.indexer_workspace_bytes(99, 4, 100, 8) == 0
     assert lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, 4, 100, 0) == 0
 
@@ -172,3 +175,29 @@ def test_error_string_is_thread_local():
     t.join()
     assert "n_vec" in out["t"]
     assert err(lib) == ""
+
+
+def test_translate_validation():
+    lib = dsa.load_library()
+    f = lib.indexer_translate
+    ok = dict(idx=FAKE, ld_idx=8, k=8, cache=cache(), rows=rows(), slots=FAKE, ld_slots=8)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["idx"], a["ld_idx"], a["k"], a["cache"], a["rows"], a["slots"], a["ld_slots"], None)
+
+    assert call(k=-1) == dsa.IDX_EINVAL
+    assert call(ld_idx=7) == dsa.IDX_EINVAL
+    assert call(ld_slots=7) == dsa.IDX_EINVAL
+    assert call(cache=cache(bs=16)) == dsa.IDX_EUNSUPPORTED
+    assert call(cache=cache(nb=0)) == dsa.IDX_EINVAL
+    assert call(idx=None) == dsa.IDX_EINVAL
+    assert call(slots=None) == dsa.IDX_EINVAL
+    assert call(idx=FAKE + 2) == dsa.IDX_EINVAL and "idx" in err(lib)
+    assert call(slots=FAKE + 4) == dsa.IDX_EINVAL and "slots" in err(lib)
+    # the cache base is not read: NULL is accepted by validation (checked here with a
+    # misaligned slots pointer, so nothing is launched)
+    assert call(cache=cache(base=None), slots=FAKE + 4) == dsa.IDX_EINVAL and "slots" in err(lib)
+    # nothing to do: no launch, no pointer needed
+    assert call(k=0, idx=None, slots=None) == dsa.IDX_OK
+    assert call(rows=rows(n=0), idx=None, slots=None) == dsa.IDX_OK
