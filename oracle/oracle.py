@@ -32,6 +32,11 @@ tests/test_oracle_*.py):
   q_prep .................................... pinned (per-vector brute force, the
                                              rotation identities, RoPE's relative-
                                              position property)
+  e2m1_decode, e2m1_encode, quant_mxfp4,
+  dequant_mxfp4 ............................ pinned (OCP value table, exact-rational
+                                             nearest-value brute force, the block
+                                             exponent's defining inequality, error
+                                             bound, a hand-worked block)
   score, score_rows ....................... pinned (exact-rational brute force,
                                              closed forms, invariants)
   topk ..................................... pinned (subset brute force, numpy and
@@ -153,6 +158,73 @@ def quant_fp8(x) -> tuple[np.ndarray, np.ndarray]:
 def dequant_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """float64 value of quantised vectors: scale * decode(code), exact."""
     return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+# ----------------------------------------------------------------------------------
+# fp4 index keys.  The pages name an fp4 variant of the indexer key only as a call,
+# fp4_act_quant_inplace(kv, 32), applied after the rotation, and as "the fp4 QAT
+# round-trip" ([ATOM-1507] "Where" and "Recommended fix").  READING: OCP MXFP4, the
+# microscaling format with 32-element blocks: e2m1 elements (1 sign, 2 exponent bits
+# with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) sharing one e8m0
+# scale 2^(E-127) per block.  The shared exponent is floor(log2(amax)) - 2 (2 being
+# the largest e2m1 exponent), limited to the e8m0 range [-127, 127]; each element is
+# x / 2^e rounded to the nearest e2m1 value, ties to the even mantissa, saturating at
+# +-6.  An all-zero block takes the scale 2^0.  The round trip through these codes
+# is the QAT round trip, so storing the codes and widening them at read time gives
+# the same values.
+# ----------------------------------------------------------------------------------
+
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each 4-bit e2m1 code (bit 3 = sign) as float64."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = np.asarray(E2M1_MAGNITUDES)[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_encode(v) -> np.ndarray:
+    """Nearest e2m1 code of each value: ties to the code with an even mantissa bit,
+    saturating at +-6, the sign kept (-0 gives code 8).  The comparison with the
+    midpoint of the two neighbouring magnitudes is exact in float64."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.isnan(v).any():
+        raise ValueError("e2m1_encode: NaN input")
+    a = np.abs(v)
+    table = np.asarray(E2M1_MAGNITUDES)
+    hi = np.minimum(np.searchsorted(table, a, side="left"), 7)   # first magnitude >= a
+    lo = np.maximum(hi - 1, 0)
+    mid = (table[lo] + table[hi]) / 2.0
+    pick_hi = (table[hi] == a) | (a > mid) | ((a == mid) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a > 6.0, 7, code)
+    return (code | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def quant_mxfp4(x, block: int = 32) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP4 quantisation of rows of 128 values in blocks of `block` (the reading
+    above).  Returns (codes uint8 [..., 128] holding one 4-bit code each,
+    e8m0 uint8 [..., 128 // block] biased exponents)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    shp = x.shape
+    xb = x.reshape(shp[:-1] + (shp[-1] // block, block))
+    amax = np.abs(xb).max(axis=-1)
+    # floor(log2(amax)) from the exact binary exponent (np.log2 may round up just
+    # below a power of two): frexp gives amax = m * 2^q with m in [0.5, 1)
+    _, q = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.where(amax > 0, (q - 1) - 2, 0)
+    e = np.clip(e, -127, 127)
+    codes = e2m1_encode(xb / np.ldexp(1.0, e)[..., None])
+    return codes.reshape(shp), (e + 127).astype(np.uint8)
+
+
+def dequant_mxfp4(codes, e8m0, block: int = 32) -> np.ndarray:
+    c = np.asarray(codes)
+    shp = c.shape
+    vals = e2m1_decode(c).reshape(shp[:-1] + (shp[-1] // block, block))
+    scale = np.ldexp(1.0, np.asarray(e8m0, dtype=np.int64) - 127)
+    return (vals * scale[..., None]).reshape(shp)
 
 
 # ----------------------------------------------------------------------------------
