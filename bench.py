@@ -43,6 +43,7 @@ WORKLOADS = {
     "tiny_decode": (1, "bf16", "decode 1 x 2000, bf16 keys, top-512"),
     "ab_bf16": (3, "bf16", "decode 16 x 131072, bf16 keys, top-1024"),
     "ab_fp8": (3, "fp8", "decode 16 x 131072, fp8 keys, top-1024"),
+    "ab_fp4": (3, "fp4", "decode 16 x 131072, MXFP4 keys (e2m1 + e8m0 per 32), top-1024"),
     "prefill": (4, "fp8", "chunked prefill 4096 rows on a 32768 prefix, fp8 keys, top-1024"),
     "long_decode": (5, "fp8", "decode 4 x 1048576 fp8 keys after a 4096-token store, top-1024"),
 }
@@ -86,7 +87,7 @@ class Runner:
         wl = gen.config(cfg, key_dtype=kd)
         self.wl, self.kd = wl, kd
         dev = "cuda"
-        self.dtype = dsa.IDX_BF16 if kd == "bf16" else dsa.IDX_FP8_E4M3
+        self.dtype = {"bf16": dsa.IDX_BF16, "fp8": dsa.IDX_FP8_E4M3, "fp4": dsa.IDX_MXFP4}[kd]
         cbytes = dsa.cache_bytes(self.dtype, wl.block_size, wl.num_blocks)
         self.replicas = replicas or max(1, -(-COLD_BYTES // cbytes))
 
@@ -153,7 +154,7 @@ class Runner:
             flops = 2.0 * wl.heads * 128 * keys
             return {"bound": "mfma", "unit": "TFLOP/s", "work": flops, "peak": FP8_MFMA_PEAK_TFLOPS,
                     "kernel": "score_prefill"}
-        key_bytes = 132 if self.kd == "fp8" else 256
+        key_bytes = {"fp8": 132, "fp4": 68, "bf16": 256}[self.kd]
         per_key = key_bytes + 4 + 4.0 / wl.block_size          # key, score write, table entry
         per_row = wl.heads * 128 * 2 + wl.heads * 4 + 8         # q (bf16), w, row_seq + row_len
         pad = sum(wl.max_row_len - int(n) for n in wl.row_len) * 4   # -inf padding writes
@@ -307,6 +308,8 @@ def cpu_baseline(wl, kd, budget_s=15.0, min_s=10.0):
                 x = wl.keys_bits[b]
                 if kd == "fp8":
                     prefix_cache[b] = O.quant_fp8(O.bf16_bits_to_f32(x))
+                elif kd == "fp4":
+                    prefix_cache[b] = O.quant_mxfp4(O.bf16_bits_to_f32(x))
                 else:
                     prefix_cache[b] = x
             t0 = time.perf_counter()
@@ -316,11 +319,20 @@ def cpu_baseline(wl, kd, budget_s=15.0, min_s=10.0):
             nstored = int(wl.stored_len[b])
             for p0 in range(0, min(n, nstored), 1 << 16):
                 p1 = min(n, nstored, p0 + (1 << 16))
-                parts.append(O.dequant_fp8(store[0][p0:p1], store[1][p0:p1]) if kd == "fp8"
-                             else O.bf16_bits_to_f64(store[p0:p1]))
+                if kd == "fp8":
+                    parts.append(O.dequant_fp8(store[0][p0:p1], store[1][p0:p1]))
+                elif kd == "fp4":
+                    parts.append(O.dequant_mxfp4(store[0][p0:p1], store[1][p0:p1]))
+                else:
+                    parts.append(O.bf16_bits_to_f64(store[p0:p1]))
             if n > nstored:
                 y = O.store_chain(wl.new_x_bits[sel], wl.new_pos[sel], 7, wl.rms_eps, wl.rope_base, wl.rope_dim)
-                parts.append(O.dequant_fp8(*O.quant_fp8(y.astype(np.float32))) if kd == "fp8" else y)
+                if kd == "fp8":
+                    parts.append(O.dequant_fp8(*O.quant_fp8(y.astype(np.float32))))
+                elif kd == "fp4":
+                    parts.append(O.dequant_mxfp4(*O.quant_mxfp4(y.astype(np.float32))))
+                else:
+                    parts.append(y)
             keys = np.concatenate(parts, 0)[:n]
             q = O.bf16_bits_to_f64(wl.q_bits[r])
             if wl.q_dtype == "fp8":
@@ -428,7 +440,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not run.prefill else "fp8",
+        "dtype": "fp8" if run.prefill else "bf16",
         "data": "synthetic",
         "config": {
             "workload": args.workload,

@@ -53,7 +53,7 @@ typedef enum {
   IDX_EWORKSPACE = -4     /* workspace missing or smaller than required */
 } idx_status;
 
-typedef enum { IDX_BF16 = 1, IDX_FP8_E4M3 = 2 } idx_dtype;
+typedef enum { IDX_BF16 = 1, IDX_FP8_E4M3 = 2, IDX_MXFP4 = 3 } idx_dtype;
 
 /* index_k_store flags: which steps precede the quantise-and-scatter.  flags = 0
  * stores the input as given (quantised for an fp8 cache). */
@@ -73,6 +73,14 @@ enum { IDX_OP_TOPK = 1, IDX_OP_SCORE_TOPK = 2 };
  *                 base + b*block_size*132: first block_size*128 bytes of OCP e4m3fn
  *                 codes (row-major, 128 per token), then block_size fp32 scales.
  *                 Token value = scale * decode(code).
+ *               IDX_MXFP4 (the fp4 index keys of [ATOM-1507] "Where",
+ *                 fp4_act_quant_inplace(kv, 32), read as OCP MXFP4): block b is
+ *                 block_size*68 bytes at base + b*block_size*68: first
+ *                 block_size*64 bytes of e2m1 codes (64 per token; element 2i in
+ *                 the low nibble of byte i), then block_size*4 e8m0 bytes (the
+ *                 scale 2^(E-127) of token elements 32j .. 32j+31 is byte 4t+j).
+ *                 Scored with bf16 queries only (indexer_score); fp8 queries
+ *                 against MXFP4 keys return IDX_EUNSUPPORTED.
  *   block_size  tokens per block: 32 or 64.
  *   num_blocks  blocks in the pool (physical block ids are in [0, num_blocks)).
  */
@@ -117,7 +125,11 @@ typedef struct {
  *   Hadamard  y = H y / sqrt(128), H the 128x128 Sylvester-order Walsh matrix
  *   store     fp8 cache: amax = max|y|, s = amax/448 (correctly rounded fp32
  *             division; s = 1 when amax < 2^-100), code = e4m3(y/s) rounded to
- *             nearest even with saturation; bf16 cache: y rounded to nearest even.
+ *             nearest even with saturation; bf16 cache: y rounded to nearest even;
+ *             MXFP4 cache: per 32-element block, e = floor(log2(amax)) - 2 within
+ *             [-127, 127] (0 for an all-zero block), codes = e2m1(y * 2^-e) to the
+ *             nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even mantissa bit,
+ *             saturating at 6), e8m0 byte e + 127.
  * Arguments:
  *   x_bf16        device bf16 [n][128] hidden rows (row-major).
  *   n             number of tokens (0 is a no-op).

@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")
 
 IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_ELAUNCH, IDX_EWORKSPACE = 0, -1, -2, -3, -4
-IDX_BF16, IDX_FP8_E4M3 = 1, 2
+IDX_BF16, IDX_FP8_E4M3, IDX_MXFP4 = 1, 2, 3
 IDX_STORE_RMSNORM, IDX_STORE_ROPE, IDX_STORE_HADAMARD = 1, 2, 4
 IDX_STORE_ALL = 7
 IDX_OP_TOPK, IDX_OP_SCORE_TOPK = 1, 2
@@ -111,14 +111,19 @@ def kcache(buf, dtype: int, block_size: int, num_blocks: int) -> KCache:
     """Describe a paged cache held in the uint8 device tensor `buf`."""
     import torch
     _need(buf, torch.uint8, "cache buffer")
-    per_block = block_size * (256 if dtype == IDX_BF16 else 132)
+    per_block = block_size * token_bytes(dtype)
     if buf.numel() < per_block * num_blocks:
         raise ValueError("cache buffer smaller than num_blocks blocks")
     return KCache(buf.data_ptr(), dtype, block_size, num_blocks)
 
 
+def token_bytes(dtype: int) -> int:
+    """Cache bytes per token: bf16 256, fp8 128 codes + 4 scale, MXFP4 64 codes + 4 scales."""
+    return {IDX_BF16: 256, IDX_FP8_E4M3: 132, IDX_MXFP4: 68}[dtype]
+
+
 def cache_bytes(dtype: int, block_size: int, num_blocks: int) -> int:
-    return block_size * (256 if dtype == IDX_BF16 else 132) * num_blocks
+    return block_size * token_bytes(dtype) * num_blocks
 
 
 def rows_desc(block_table, row_seq, row_len, max_row_len: int) -> Rows:

@@ -35,8 +35,8 @@ constexpr int32_t kHeadsV1 = 64;
 int32_t check_cache(const idx_kcache& c) {
   if (!c.base) return fail(IDX_EINVAL, "cache.base is NULL");
   if (!aligned(c.base, 256)) return fail(IDX_EINVAL, "cache.base must be 256-byte aligned");
-  if (c.dtype != IDX_BF16 && c.dtype != IDX_FP8_E4M3)
-    return fail(IDX_EINVAL, "cache.dtype %d is not IDX_BF16 or IDX_FP8_E4M3", c.dtype);
+  if (c.dtype != IDX_BF16 && c.dtype != IDX_FP8_E4M3 && c.dtype != IDX_MXFP4)
+    return fail(IDX_EINVAL, "cache.dtype %d is not IDX_BF16, IDX_FP8_E4M3 or IDX_MXFP4", c.dtype);
   if (c.block_size != 32 && c.block_size != 64)
     return fail(IDX_EUNSUPPORTED, "cache.block_size %d unsupported (32 or 64)", c.block_size);
   if (c.num_blocks < 1) return fail(IDX_EINVAL, "cache.num_blocks must be >= 1");
@@ -63,8 +63,8 @@ int32_t check_score_args(const void* q, int32_t q_dtype, const float* q_scale, c
   if (heads != kHeadsV1) return fail(IDX_EUNSUPPORTED, "heads=%d unsupported (64)", heads);
   if (q_dtype != IDX_BF16 && q_dtype != IDX_FP8_E4M3)
     return fail(IDX_EINVAL, "q_dtype %d is not IDX_BF16 or IDX_FP8_E4M3", q_dtype);
-  if (q_dtype == IDX_FP8_E4M3 && cache.dtype == IDX_BF16)
-    return fail(IDX_EUNSUPPORTED, "fp8 queries against bf16 keys are not supported");
+  if (q_dtype == IDX_FP8_E4M3 && cache.dtype != IDX_FP8_E4M3)
+    return fail(IDX_EUNSUPPORTED, "fp8 queries are supported against fp8 keys only");
   if (rows.rows == 0) return IDX_OK;
   if (!q || !w) return fail(IDX_EINVAL, "q and w must be non-NULL");
   if (!aligned(q, 16)) return fail(IDX_EINVAL, "q must be 16-byte aligned");

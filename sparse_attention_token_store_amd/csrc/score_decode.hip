@@ -1,5 +1,6 @@
 // Decode scoring: one bf16 query row (64 index heads x 128) against the paged
-// index-K cache (bf16 keys, or fp8 e4m3 keys with a per-token fp32 scale):
+// index-K cache (bf16 keys, fp8 e4m3 keys with a per-token fp32 scale, or MXFP4 keys:
+// e2m1 codes with an e8m0 scale per 32 dims):
 //     score[p] = s_p * sum_h w_h * max(0, q_h . k_p)
 // (the lightning-indexer q.k score of ROCm/ATOM issue 1507, "Root cause found"; the
 // paged read through the block table is the analog of the pages'
@@ -17,10 +18,15 @@
 //    products are unchanged.
 //  - fp8 keys (score_decode_fp8_kernel) stream through a per-wave LDS ring filled by
 //    LDS DMA, which keeps two 16-key groups in flight without holding VGPRs
-//    (4 waves per SIMD).  bf16 keys (score_decode_kernel) load each 64-key span
-//    straight into registers with the next span prefetched.
+//    (4 waves per SIMD).  bf16 and MXFP4 keys (score_decode_kernel) load each 64-key
+//    span straight into registers with the next span prefetched.
 //  - fp8 codes are widened to bf16 exactly (every e4m3 value is a bf16 value) with
 //    v_cvt_scalef32_pk_bf16_fp8; the per-key scale multiplies the head sum.
+//  - MXFP4: lane l's 32 contiguous dims 32*(l/16) .. +31 are exactly one 32-element
+//    scale block of its key, so the lane widens its 16 code bytes with
+//    v_cvt_scalef32_pk_bf16_fp4 and the block's power-of-two scale folded in
+//    (e2m1 * 2^k is a bf16 value; the conversion uses the scale's exponent, and
+//    reproduces every e2m1 * 2^k for k in [-127, 121] exactly on the hardware).
 //  - The ReLU-weighted head sum is in-lane (16 of the 64 heads per lane) plus two
 //    cross-lane adds; lane l ends up with the score of key l%16 of its group, and
 //    64 scores at a time leave with one coalesced 256-byte write.
@@ -32,42 +38,54 @@ namespace {
 
 constexpr int kSpan = 64;  // keys per span (one 64-token block, or two 32-token blocks)
 
-template <bool kFp8>
+enum KeyKind { kBf16Keys = 0, kFp8Keys = 1, kFp4Keys = 2 };
+
+// Keys per wave span of the register kernel (a multiple of 64).  MXFP4 keys use
+// 64-key spans too: measured on 16 x 131072 keys, 128- and 192-key spans (more bytes
+// in flight, more VGPRs) were 6% and 16% slower; the kernel is bound by the per-group
+// widening and MFMA work at 2 waves per SIMD, not by loads in flight.
+#ifndef DSA_FP4_SPAN
+#define DSA_FP4_SPAN 64
+#endif
+template <int kKeys>
+constexpr int span_keys() { return kKeys == kFp4Keys ? DSA_FP4_SPAN : 64; }
+
+template <int kKeys>
 struct SpanRaw;
 template <>
-struct SpanRaw<true> {
-  uint4 c[4][2];  // per 16-key group: 32 code bytes of this lane's key
-  float s[4];     // per group: scale of this lane's key
-};
-template <>
-struct SpanRaw<false> {
+struct SpanRaw<kBf16Keys> {
   uint4 c[4][4];  // per 16-key group: 64 bytes (32 bf16) of this lane's key
 };
+template <>
+struct SpanRaw<kFp4Keys> {
+  uint4 c[DSA_FP4_SPAN / 16];     // per 16-key group: 16 code bytes (32 e2m1) of this lane's key
+  uint32_t e[DSA_FP4_SPAN / 64];  // per group g: e8m0 byte of this lane's block, byte g % 4
+};
 
-// Loads the keys of one 64-key span for this lane.  Groups at or past the row's
-// length are not touched (their block-table entries may not exist); a block id
-// outside the pool marks the span bad and reads block 0 instead.
-template <bool kFp8, int BS>
-__device__ __forceinline__ void load_span(SpanRaw<kFp8>& raw, bool& bad, const uint8_t* cache,
+// Loads the keys of one span for this lane.  Groups at or past the row's length are
+// not touched (their block-table entries may not exist); a block id outside the pool
+// sets the group's bit in `bad` and reads block 0 instead.
+template <int kKeys, int BS>
+__device__ __forceinline__ void load_span(SpanRaw<kKeys>& raw, uint32_t& bad, const uint8_t* cache,
                                           int64_t num_blocks, const int32_t* bt_row, int p_span,
                                           int n, int lane) {
-  bad = false;
+  bad = 0;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < span_keys<kKeys>() / 16; ++g) {
     const int p0 = p_span + 16 * g;
     if (p0 >= n) continue;  // uniform per wave
     int phys = bt_row[p0 / BS];
     if (phys < 0 || phys >= num_blocks) {
-      bad = true;
+      bad |= 1u << g;
       phys = 0;
     }
     const int off = (p0 % BS) + (lane & 15);
-    if constexpr (kFp8) {
-      const uint8_t* blk = cache + (int64_t)phys * (BS * 132);
-      const uint4* src = reinterpret_cast<const uint4*>(blk + off * 128 + 32 * (lane >> 4));
-      raw.c[g][0] = src[0];
-      raw.c[g][1] = src[1];
-      raw.s[g] = reinterpret_cast<const float*>(blk + BS * 128)[off];
+    if constexpr (kKeys == kFp4Keys) {
+      const uint8_t* blk = cache + (int64_t)phys * (BS * 68);
+      raw.c[g] = *reinterpret_cast<const uint4*>(blk + off * 64 + 16 * (lane >> 4));
+      const uint32_t e8 = blk[BS * 64 + off * 4 + (lane >> 4)];
+      if (g % 4 == 0) raw.e[g / 4] = 0;
+      raw.e[g / 4] |= e8 << (8 * (g % 4));
     } else {
       const uint4* src = reinterpret_cast<const uint4*>(cache + ((int64_t)phys * BS + off) * 256 +
                                                         64 * (lane >> 4));
@@ -89,6 +107,20 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return u.v;
 }
 
+// 8 e2m1 codes (element 2i in the low nibble of byte i) -> 8 bf16 values, times the
+// power-of-two scale
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t d, float scale) {
+  union {
+    bf16x2_t h[4];
+    bf16x8_t v;
+  } u;
+  u.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0);
+  u.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1);
+  u.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2);
+  u.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
+  return u.v;
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   union {
     uint4 u;
@@ -98,7 +130,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return x.b;
 }
 
-template <bool kFp8, int BS>
+template <int kKeys, int BS>
 __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
     int64_t num_blocks, const int32_t* __restrict__ block_table, int max_blocks, int num_seqs,
@@ -110,11 +142,12 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
   const int seq = row_seq[r];
   const int n = min(max(row_len[r], 0), max_row_len);
   float* out = scores + (int64_t)r * ld;
-  const int chunk0 = blockIdx.x * (4 * spans_per_wave * kSpan);
+  constexpr int KS = span_keys<kKeys>();
+  const int chunk0 = blockIdx.x * (4 * spans_per_wave * KS);
   const bool seq_bad = seq < 0 || seq >= num_seqs;
 
   if (chunk0 >= n || seq_bad) {  // nothing to read: padding, or NaN for a bad sequence
-    const int end = min(chunk0 + 4 * spans_per_wave * kSpan, max_row_len);
+    const int end = min(chunk0 + 4 * spans_per_wave * KS, max_row_len);
     for (int p = chunk0 + (int)threadIdx.x; p < end; p += 256) {
       if (p < n) out[p] = __builtin_nanf("");
       else if (write_pad) out[p] = -INFINITY;
@@ -142,52 +175,60 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
 
   const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
 
-  SpanRaw<kFp8> cur, nxt;
-  bool cur_bad = false, nxt_bad = false;
-  int p_span = chunk0 + wave * kSpan;
-  if (p_span < n) load_span<kFp8, BS>(cur, cur_bad, cache, num_blocks, bt_row, p_span, n, lane);
+  SpanRaw<kKeys> cur, nxt;
+  uint32_t cur_bad = 0, nxt_bad = 0;
+  int p_span = chunk0 + wave * KS;
+  if (p_span < n) load_span<kKeys, BS>(cur, cur_bad, cache, num_blocks, bt_row, p_span, n, lane);
 
-  for (int i = 0; i < spans_per_wave; ++i, p_span += 4 * kSpan) {
-    const int p_next = p_span + 4 * kSpan;
+  for (int i = 0; i < spans_per_wave; ++i, p_span += 4 * KS) {
+    const int p_next = p_span + 4 * KS;
     if (i + 1 < spans_per_wave && p_next < n)
-      load_span<kFp8, BS>(nxt, nxt_bad, cache, num_blocks, bt_row, p_next, n, lane);
+      load_span<kKeys, BS>(nxt, nxt_bad, cache, num_blocks, bt_row, p_next, n, lane);
 
     if (p_span < n) {
-      float val = 0.0f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4_t acc[4];
+      for (int sub = 0; sub < KS / 64; ++sub) {  // 64 keys: four 16-key groups
+        float val = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < 4; ++g) {
+          const int gg = 4 * sub + g;
+          f32x4_t acc[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8_t b;
-          if constexpr (kFp8) {
-            const uint4 c = cur.c[g][s >> 1];
-            b = (s & 1) ? fp8x8_to_bf16x8(c.z, c.w) : fp8x8_to_bf16x8(c.x, c.y);
-          } else {
-            b = as_bf16x8(cur.c[g][s]);
+          for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            bf16x8_t b;
+            if constexpr (kKeys == kFp4Keys) {
+              const uint4 c = cur.c[gg];
+              const uint32_t d = s == 0 ? c.x : (s == 1 ? c.y : (s == 2 ? c.z : c.w));
+              const uint32_t e8 = (cur.e[gg / 4] >> (8 * (gg % 4))) & 0xFFu;
+              b = fp4x8_to_bf16x8(d, __uint_as_float(e8 ? e8 << 23 : 0x00400000u));  // 2^(e8-127)
+            } else {
+              b = as_bf16x8(cur.c[gg][s]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], b, acc[mt], 0, 0, 0);
           }
+          float part = 0.0f;
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], b, acc[mt], 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) part = fmaf(wv[mt][v], relu(acc[mt][v]), part);
+          part = rows4_sum(part);
+          if ((lane >> 4) == g) val = part + 0.0f;  // +0.0f: a zero score is +0
         }
-        float part = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) part = fmaf(wv[mt][v], relu(acc[mt][v]), part);
-        part = rows4_sum(part);
-        if constexpr (kFp8) part *= cur.s[g];
-        if ((lane >> 4) == g) val = part + 0.0f;  // +0.0f: a zero score is +0
+        const int p = p_span + 64 * sub + lane;
+        if (p >= n) val = -INFINITY;
+        if ((cur_bad >> (4 * sub + (lane >> 4))) & 1u) val = __builtin_nanf("");
+        if (p < max_row_len) out[p] = val;
       }
-      const int p = p_span + lane;
-      if (p >= n) val = -INFINITY;
-      if (cur_bad) val = __builtin_nanf("");
-      if (p < max_row_len) out[p] = val;
     } else if (write_pad) {
-      const int p = p_span + lane;
-      if (p < max_row_len) out[p] = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < KS / 64; ++sub) {
+        const int p = p_span + 64 * sub + lane;
+        if (p < max_row_len) out[p] = -INFINITY;
+      }
     }
     cur = nxt;
     cur_bad = nxt_bad;
@@ -356,17 +397,18 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
     }
 }
 
-template <bool kFp8>
+template <int kKeys>
 hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const Rows& r,
                      float* scores, int64_t ld, bool write_pad, hipStream_t s) {
-  const int64_t spans_row = (r.max_row_len + kSpan - 1) / kSpan;
+  constexpr int KS = kKeys == kFp8Keys ? kSpan : span_keys<kKeys>();
+  const int64_t spans_row = (r.max_row_len + KS - 1) / KS;
   const int64_t total = spans_row * r.rows;
   // aim for >= ~4 workgroups per CU on the 256-CU part, at most 8 spans per wave
   int spw = (int)(total / (4 * 1024));
   spw = spw < 1 ? 1 : (spw > 8 ? 8 : spw);
   const int64_t per_wg = 4LL * spw;
   const dim3 grid((unsigned)((spans_row + per_wg - 1) / per_wg), (unsigned)r.rows), block(256);
-  if constexpr (kFp8) {
+  if constexpr (kKeys == kFp8Keys) {  // fp8 keys: the LDS-ring kernel
     if (c.block_size == 64)
       hipLaunchKernelGGL((score_decode_fp8_kernel<64, kDecodeRing>), grid, block, 0, s, q, w, c.base,
                          c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
@@ -375,13 +417,13 @@ hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const R
       hipLaunchKernelGGL((score_decode_fp8_kernel<32, kDecodeRing>), grid, block, 0, s, q, w, c.base,
                          c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
                          r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
-  } else {  // bf16 keys: the register-streaming kernel
+  } else {  // bf16 or MXFP4 keys: the register-streaming kernel
     if (c.block_size == 64)
-      hipLaunchKernelGGL((score_decode_kernel<false, 64>), grid, block, 0, s, q, w, c.base,
+      hipLaunchKernelGGL((score_decode_kernel<kKeys, 64>), grid, block, 0, s, q, w, c.base,
                          c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
                          r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
     else
-      hipLaunchKernelGGL((score_decode_kernel<false, 32>), grid, block, 0, s, q, w, c.base,
+      hipLaunchKernelGGL((score_decode_kernel<kKeys, 32>), grid, block, 0, s, q, w, c.base,
                          c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
                          r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
   }
@@ -393,8 +435,9 @@ hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const R
 hipError_t launch_score_decode(const uint16_t* q, const float* w, const KCache& c, const Rows& r,
                                float* scores, int64_t ld, bool write_pad, hipStream_t s) {
   if (r.rows == 0 || r.max_row_len == 0) return hipSuccess;
-  return c.dtype == 2 ? launch_bs<true>(q, w, c, r, scores, ld, write_pad, s)
-                      : launch_bs<false>(q, w, c, r, scores, ld, write_pad, s);
+  if (c.dtype == 2) return launch_bs<kFp8Keys>(q, w, c, r, scores, ld, write_pad, s);
+  if (c.dtype == 3) return launch_bs<kFp4Keys>(q, w, c, r, scores, ld, write_pad, s);
+  return launch_bs<kBf16Keys>(q, w, c, r, scores, ld, write_pad, s);
 }
 
 }  // namespace dsa

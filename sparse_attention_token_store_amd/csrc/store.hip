@@ -163,7 +163,33 @@ __device__ __forceinline__ void quantise8(const float (&f)[8], uint32_t& lo, uin
   hi = e4m3_encode2(q[4], q[5]) | (e4m3_encode2(q[6], q[7]) << 16);
 }
 
-template <bool kFp8>
+// e2m1 code of v (bit 3 = sign): the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to
+// the even mantissa bit, saturating at 6.  Counting the thresholds passed, strict at
+// the ties that round down (0.25, 1.25, 2.5, 5) and inclusive at those that round up
+// (0.75, 1.75, 3.5), gives the code directly.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// MXFP4 quantisation of the vector held as (y0, y1) pairs across the wave: the 16
+// lanes of DPP row g hold the 32-element block g.  Shared exponent
+// e = floor(log2(amax)) - 2 within [-127, 127] (0 for an all-zero block); codes of
+// y * 2^-e (exact: a power-of-two scaling).  Returns this lane's code byte (element
+// 2*lane in the low nibble) and the block's e8m0 byte e + 127.
+__device__ __forceinline__ uint32_t quantise_mxfp4_pair(float y0, float y1, uint32_t& e8) {
+  const float amax = row16_max(fmaxf(fabsf(y0), fabsf(y1)));
+  int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 2 : 0;
+  e = min(max(e, -127), 127);
+  e8 = (uint32_t)(e + 127);
+  return e2m1_code(ldexpf(y0, -e)) | (e2m1_code(ldexpf(y1, -e)) << 4);
+}
+
+// kKind: 0 bf16 cache, 1 fp8 (e4m3 + fp32 scale), 2 MXFP4 (e2m1 + e8m0 per 32)
+template <int kKind>
 __global__ __launch_bounds__(256) void index_k_store_kernel(
     const uint16_t* __restrict__ x, int64_t n, const int32_t* __restrict__ pos,
     const int64_t* __restrict__ slots, uint8_t* __restrict__ base, int bs, int64_t num_blocks,
@@ -182,12 +208,19 @@ __global__ __launch_bounds__(256) void index_k_store_kernel(
   const int64_t slot = slots[t];
   if (slot < 0 || slot >= num_blocks * bs) return;  // uniform per wave
   const int64_t blk = slot / bs, off = slot - blk * bs;
-  if constexpr (kFp8) {
+  if constexpr (kKind == 1) {
     float s;
     const uint32_t c = quantise_pair(y0, y1, s);
     uint8_t* blkp = base + blk * (int64_t)bs * 132;
     reinterpret_cast<uint16_t*>(blkp + off * kHeadDim)[lane] = (uint16_t)c;
     if (lane == 0) reinterpret_cast<float*>(blkp + (int64_t)bs * kHeadDim)[off] = s;
+  } else if constexpr (kKind == 2) {
+    // block layout: [bs][64] code bytes, then [bs][4] e8m0 bytes (68 B per token)
+    uint32_t e8;
+    const uint32_t c = quantise_mxfp4_pair(y0, y1, e8);
+    uint8_t* blkp = base + blk * (int64_t)bs * 68;
+    blkp[off * 64 + lane] = (uint8_t)c;
+    if ((lane & 15) == 0) blkp[(int64_t)bs * 64 + off * 4 + (lane >> 4)] = (uint8_t)e8;
   } else {
     uint32_t* dst = reinterpret_cast<uint32_t*>(base + (blk * bs + off) * 256);
     dst[lane] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
@@ -351,10 +384,13 @@ hipError_t launch_store(const uint16_t* x, int64_t n, const int32_t* pos, const 
   const double ln_step = rope_step(rope_base, rope_dim);
   const dim3 grid((unsigned)((n + 3) / 4)), block(256);
   if (c.dtype == 2)
-    hipLaunchKernelGGL(index_k_store_kernel<true>, grid, block, 0, s, x, n, pos, slots, c.base,
+    hipLaunchKernelGGL(index_k_store_kernel<1>, grid, block, 0, s, x, n, pos, slots, c.base,
+                       c.block_size, c.num_blocks, flags, eps, ln_step, rope_dim, dbg);
+  else if (c.dtype == 3)
+    hipLaunchKernelGGL(index_k_store_kernel<2>, grid, block, 0, s, x, n, pos, slots, c.base,
                        c.block_size, c.num_blocks, flags, eps, ln_step, rope_dim, dbg);
   else
-    hipLaunchKernelGGL(index_k_store_kernel<false>, grid, block, 0, s, x, n, pos, slots, c.base,
+    hipLaunchKernelGGL(index_k_store_kernel<0>, grid, block, 0, s, x, n, pos, slots, c.base,
                        c.block_size, c.num_blocks, flags, eps, ln_step, rope_dim, dbg);
   return hipGetLastError();
 }

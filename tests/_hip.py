@@ -38,7 +38,7 @@ class GpuWorkload:
     def __init__(self, wl, key_dtype: str | None = None, dev="cuda", fill=0xFF, block_table=None):
         self.wl = wl
         self.key_dtype = key_dtype or wl.key_dtype
-        self.dtype = dsa.IDX_BF16 if self.key_dtype == "bf16" else dsa.IDX_FP8_E4M3
+        self.dtype = {"bf16": dsa.IDX_BF16, "fp8": dsa.IDX_FP8_E4M3, "fp4": dsa.IDX_MXFP4}[self.key_dtype]
         nbytes = dsa.cache_bytes(self.dtype, wl.block_size, wl.num_blocks)
         # unwritten slots hold 0xFF bytes (NaN codes / NaN bf16): masked positions must
         # never leak into a visible score

@@ -23,7 +23,7 @@ import numpy as np
 
 from oracle import oracle as O
 
-RTOL = {"bf16": 1e-3, "fp8": 2e-3}
+RTOL = {"bf16": 1e-3, "fp8": 2e-3, "fp4": 2e-3}
 # bound on |float32 chain - float64 chain| relative to the row's absmax (the
 # float32 pipeline measures ~4e-7; the store test asserts 1e-5)
 CHAIN_REL_ERR = 2e-6
@@ -103,6 +103,8 @@ class OracleKeys:
         x = self.wl.keys_bits[b][p0:p1]
         if self.key_dtype == "bf16":
             return O.bf16_bits_to_f64(x)
+        if self.key_dtype == "fp4":
+            return O.dequant_mxfp4(*O.quant_mxfp4(O.bf16_bits_to_f32(x)))
         return O.dequant_fp8(*O.quant_fp8(O.bf16_bits_to_f32(x)))
 
     def __call__(self, b: int, p0: int, p1: int) -> np.ndarray:

@@ -55,7 +55,7 @@ def test_store_validation():
     assert f(FAKE, 4, None, FAKE, cache(base=ALIGNED + 16), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
     assert "aligned" in err(lib)
     assert f(FAKE, 4, None, FAKE, cache(bs=16), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EUNSUPPORTED
-    assert f(FAKE, 4, None, FAKE, cache(dtype=3), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
+    assert f(FAKE, 4, None, FAKE, cache(dtype=4), 0, 1e-6, 1e4, 64, None, None) == dsa.IDX_EINVAL
     assert f(FAKE, 4, FAKE, FAKE, cache(), dsa.IDX_STORE_ROPE, 1e-6, 1e4, 63, None, None) == dsa.IDX_EINVAL
     assert "rope_dim" in err(lib)
     assert f(FAKE, 4, FAKE, FAKE, cache(), dsa.IDX_STORE_ROPE, 1e-6, -1.0, 64, None, None) == dsa.IDX_EINVAL
@@ -122,6 +122,8 @@ def test_score_validation():
 
     assert call(h=32) == dsa.IDX_EUNSUPPORTED and "heads" in err(lib)
     assert call(qd=dsa.IDX_FP8_E4M3, c=cache(dtype=dsa.IDX_BF16), qs=FAKE) == dsa.IDX_EUNSUPPORTED
+    assert call(qd=dsa.IDX_FP8_E4M3, c=cache(dtype=dsa.IDX_MXFP4), qs=FAKE) == dsa.IDX_EUNSUPPORTED
+    assert call(c=cache(dtype=4)) == dsa.IDX_EINVAL
     assert call(qd=dsa.IDX_FP8_E4M3) == dsa.IDX_EINVAL and "q_scale" in err(lib)
     assert call(qd=7) == dsa.IDX_EINVAL
     assert call(ld=99) == dsa.IDX_EINVAL and "ld" in err(lib)

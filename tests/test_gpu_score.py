@@ -87,18 +87,19 @@ def test_rows_sharing_a_sequence():
     check_scores(got, oracle_scores(wl, OracleKeys(wl, "bf16")), wl.row_len, RTOL["bf16"])
 
 
-@pytest.mark.parametrize("case", ["bf16_keys", "fp8_keys", "fp8_prefill"])
+@pytest.mark.parametrize("case", ["bf16_keys", "fp8_keys", "fp8_prefill", "fp4_keys"])
 def test_bad_block_id_scores_nan_without_faulting(case):
     # a block id outside the pool is caught by the kernel's bounds check: the keys
     # it covers score NaN in every row that sees them, nothing is read out of bounds
-    # (one case per scoring kernel: bf16 keys, fp8 keys, fp8 queries)
+    # (one case per scoring kernel: bf16 keys, fp8 keys, fp8 queries, fp4 keys)
     wl = {"bf16_keys": lambda: gen.config(1, scale=0.2),
           "fp8_keys": lambda: gen.config(2, scale=0.05),
-          "fp8_prefill": lambda: gen.config(4, scale=0.02)}[case]()
+          "fp8_prefill": lambda: gen.config(4, scale=0.02),
+          "fp4_keys": lambda: gen.config(3, scale=0.01)}[case]()
     seq = int(wl.row_seq[0])
     bt = wl.block_table.copy()
     bt[seq, 1] = wl.num_blocks + 5
-    g = GpuWorkload(wl, block_table=bt)
+    g = GpuWorkload(wl, block_table=bt, key_dtype="fp4" if case == "fp4_keys" else None)
     if case == "fp8_prefill":
         g.quantise_q()
         got = gpu_scores(g, fp8_q=True)
