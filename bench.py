@@ -45,6 +45,7 @@ WORKLOADS = {
     "ab_fp8": (3, "fp8", "decode 16 x 131072, fp8 keys, top-1024"),
     "ab_fp4": (3, "fp4", "decode 16 x 131072, MXFP4 keys (e2m1 + e8m0 per 32), top-1024"),
     "prefill": (4, "fp8", "chunked prefill 4096 rows on a 32768 prefix, fp8 keys, top-1024"),
+    "prefill_fp4": (4, "fp4", "chunked prefill 4096 rows on a 32768 prefix, MXFP4 keys, top-1024"),
     "long_decode": (5, "fp8", "decode 4 x 1048576 fp8 keys after a 4096-token store, top-1024"),
 }
 

@@ -79,8 +79,8 @@ enum { IDX_OP_TOPK = 1, IDX_OP_SCORE_TOPK = 2 };
  *                 block_size*64 bytes of e2m1 codes (64 per token; element 2i in
  *                 the low nibble of byte i), then block_size*4 e8m0 bytes (the
  *                 scale 2^(E-127) of token elements 32j .. 32j+31 is byte 4t+j).
- *                 Scored with bf16 queries only (indexer_score); fp8 queries
- *                 against MXFP4 keys return IDX_EUNSUPPORTED.
+ *                 Scored with bf16 queries (widened exactly to bf16) or fp8
+ *                 queries (the e8m0 bytes are the scaled MFMA's block scales).
  *   block_size  tokens per block: 32 or 64.
  *   num_blocks  blocks in the pool (physical block ids are in [0, num_blocks)).
  */

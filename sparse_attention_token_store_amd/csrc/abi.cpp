@@ -63,8 +63,8 @@ int32_t check_score_args(const void* q, int32_t q_dtype, const float* q_scale, c
   if (heads != kHeadsV1) return fail(IDX_EUNSUPPORTED, "heads=%d unsupported (64)", heads);
   if (q_dtype != IDX_BF16 && q_dtype != IDX_FP8_E4M3)
     return fail(IDX_EINVAL, "q_dtype %d is not IDX_BF16 or IDX_FP8_E4M3", q_dtype);
-  if (q_dtype == IDX_FP8_E4M3 && cache.dtype != IDX_FP8_E4M3)
-    return fail(IDX_EUNSUPPORTED, "fp8 queries are supported against fp8 keys only");
+  if (q_dtype == IDX_FP8_E4M3 && cache.dtype == IDX_BF16)
+    return fail(IDX_EUNSUPPORTED, "fp8 queries against bf16 keys are not supported");
   if (rows.rows == 0) return IDX_OK;
   if (!q || !w) return fail(IDX_EINVAL, "q and w must be non-NULL");
   if (!aligned(q, 16)) return fail(IDX_EINVAL, "q must be 16-byte aligned");

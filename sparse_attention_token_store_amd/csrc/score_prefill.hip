@@ -35,6 +35,11 @@
 //    (3 permlane swaps) and one per-key scale, so lane l holds key l of the span.
 //  - A workgroup whose rows read different sequences falls back to per-wave direct
 //    loads (correct, slower; chunked prefill never takes it).
+//  - MXFP4 keys (e2m1 codes + an e8m0 scale per 32 dims) take the same path with the
+//    MFMA's B format set to fp4: a lane's 32 contiguous dims are one scale block, so
+//    its key's e8m0 byte for that block is the lane's B scale operand and the
+//    per-key factor of the epilogue is 1 (NaN for a key of a bad block id).  Staged
+//    key rows are 64 bytes padded to 80 (80/16 odd: still 16 distinct bank groups).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -47,9 +52,12 @@ constexpr int kThreadsPf = 64 * kWavesPf;
 constexpr int kKeyChunks = 8;
 constexpr int kStageKeys = 256;                         // keys per LDS stage
 constexpr int kStageGroups = kStageKeys / 16;
-constexpr int kRowPitch = 144;                          // padded LDS key row
+constexpr int kRowPitch = 144;                          // padded LDS key row (fp8)
 constexpr int kScaleOff = kStageKeys * kRowPitch;       // scales after the key rows
 constexpr int kStage = kScaleOff + kStageKeys * 4;      // 37,888 bytes per stage
+constexpr int kRowPitch4 = 80;                          // padded LDS key row (MXFP4)
+constexpr int kScaleOff4 = kStageKeys * kRowPitch4;     // e8m0 words after the key rows
+constexpr uint32_t kBadKey = 0xFFFFFFFFu;               // staged e8m0 word of a bad block
 
 // One thread's share of a stage: code chunk tid & 7 of keys 64j + (tid >> 3), j < 4,
 // and the scale of key tid % 256 (threads 0..255 stage it).  Every thread issues the
@@ -69,12 +77,19 @@ struct ShareBlocks {
 };
 
 // (Positions are non-negative: unsigned arithmetic makes / BS and % BS shifts and masks.)
-template <int BS>
+template <int BS, bool kFp4>
 __device__ __forceinline__ ShareBlocks share_blocks(const int32_t* bt_row, int p0, int n_max, int tid) {
-  const uint32_t last = (uint32_t)n_max - 1u, k = (uint32_t)p0 + ((uint32_t)tid >> 3);
+  const uint32_t last = (uint32_t)n_max - 1u;
   const uint32_t ks = (uint32_t)p0 + ((uint32_t)tid & 255u);
-  return ShareBlocks{bt_row[min(k, last) / BS], bt_row[min(k + 64u, last) / BS], bt_row[min(k + 128u, last) / BS],
-                     bt_row[min(k + 192u, last) / BS], bt_row[min(ks, last) / BS]};
+  if constexpr (kFp4) {  // code chunk tid & 3 of keys tid >> 2 and 128 + (tid >> 2)
+    const uint32_t k = (uint32_t)p0 + ((uint32_t)tid >> 2);
+    return ShareBlocks{bt_row[min(k, last) / BS], bt_row[min(k + 128u, last) / BS], 0, 0,
+                       bt_row[min(ks, last) / BS]};
+  } else {
+    const uint32_t k = (uint32_t)p0 + ((uint32_t)tid >> 3);
+    return ShareBlocks{bt_row[min(k, last) / BS], bt_row[min(k + 64u, last) / BS], bt_row[min(k + 128u, last) / BS],
+                       bt_row[min(k + 192u, last) / BS], bt_row[min(ks, last) / BS]};
+  }
 }
 
 template <int BS>
@@ -84,11 +99,32 @@ __device__ __forceinline__ uint4 load_code(const uint8_t* cache, int64_t num_blo
                                          ((pos % BS) * 128u + ((uint32_t)tid & 7u) * 16u));
 }
 
+// MXFP4: code chunk tid & 3 (16 bytes) of the key at pos, and a key's e8m0 word
 template <int BS>
+__device__ __forceinline__ uint4 load_code4(const uint8_t* cache, int64_t num_blocks, int entry, uint32_t pos, int tid) {
+  const uint32_t phys = (entry < 0 || entry >= num_blocks) ? 0u : (uint32_t)entry;
+  return *reinterpret_cast<const uint4*>(cache + (uint64_t)phys * (BS * 68) +
+                                         ((pos % BS) * 64u + ((uint32_t)tid & 3u) * 16u));
+}
+
+template <int BS, bool kFp4>
 __device__ __forceinline__ Share load_share(const uint8_t* cache, int64_t num_blocks, const ShareBlocks& e,
                                             int p0, int n_max, int tid) {
-  const uint32_t last = (uint32_t)n_max - 1u, k = (uint32_t)p0 + ((uint32_t)tid >> 3);
+  const uint32_t last = (uint32_t)n_max - 1u;
   Share sh;
+  if constexpr (kFp4) {
+    const uint32_t k = (uint32_t)p0 + ((uint32_t)tid >> 2);
+    sh.c0 = load_code4<BS>(cache, num_blocks, e.b0, min(k, last), tid);
+    sh.c1 = load_code4<BS>(cache, num_blocks, e.b1, min(k + 128u, last), tid);
+    sh.c2 = sh.c3 = make_uint4(0, 0, 0, 0);
+    const uint32_t ps = min((uint32_t)p0 + ((uint32_t)tid & 255u), last);
+    const bool bad = e.scale < 0 || e.scale >= num_blocks;
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(cache + (uint64_t)(bad ? 0u : (uint32_t)e.scale) * (BS * 68) +
+                                                          (BS * 64u + (ps % BS) * 4u));
+    sh.scale = bad ? kBadKey : v;
+    return sh;
+  }
+  const uint32_t k = (uint32_t)p0 + ((uint32_t)tid >> 3);
   sh.c0 = load_code<BS>(cache, num_blocks, e.b0, min(k, last), tid);
   sh.c1 = load_code<BS>(cache, num_blocks, e.b1, min(k + 64u, last), tid);
   sh.c2 = load_code<BS>(cache, num_blocks, e.b2, min(k + 128u, last), tid);
@@ -102,7 +138,15 @@ __device__ __forceinline__ Share load_share(const uint8_t* cache, int64_t num_bl
   return sh;
 }
 
+template <bool kFp4>
 __device__ __forceinline__ void store_share(uint8_t* stage, const Share& sh, int tid) {
+  if constexpr (kFp4) {
+    uint8_t* p = stage + (tid >> 2) * kRowPitch4 + (tid & 3) * 16;
+    *reinterpret_cast<uint4*>(p) = sh.c0;
+    *reinterpret_cast<uint4*>(p + 128 * kRowPitch4) = sh.c1;
+    if (tid < kStageKeys) reinterpret_cast<uint32_t*>(stage + kScaleOff4)[tid] = sh.scale;
+    return;
+  }
   uint8_t* p = stage + (tid >> 3) * kRowPitch + (tid & 7) * 16;
   *reinterpret_cast<uint4*>(p) = sh.c0;
   *reinterpret_cast<uint4*>(p + 64 * kRowPitch) = sh.c1;
@@ -118,8 +162,16 @@ __device__ __forceinline__ i32x8_t read_b(const uint8_t* stage, int g, int lane)
   const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
   return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
-__device__ __forceinline__ float read_scale(const uint8_t* stage, int g, int lane) {
-  return reinterpret_cast<const float*>(stage + kScaleOff)[16 * g + (lane & 15)];
+// MXFP4: key 16g + lane%16, code bytes 16*(lane/16) .. +15 (32 e2m1, one scale block)
+__device__ __forceinline__ i32x8_t read_b4(const uint8_t* stage, int g, int lane) {
+  const uint4 c = *reinterpret_cast<const uint4*>(stage + (16 * g + (lane & 15)) * kRowPitch4 + 16 * (lane >> 4));
+  return i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+}
+// the e8m0 byte of this lane's scale block (B scale operand of the MFMA)
+__device__ __forceinline__ int scale_b4(uint32_t word, int lane) { return (int)((word >> (8 * (lane >> 4))) & 0xFFu); }
+// epilogue factor of a key from its staged e8m0 word: 1, or NaN for a bad block id
+__device__ __forceinline__ float key_factor4(uint32_t word) {
+  return word == kBadKey ? __builtin_nanf("") : 1.0f;
 }
 
 // In-lane part of the epilogue of one 16-key group: the ReLU-weighted sum over the
@@ -139,7 +191,7 @@ __device__ __forceinline__ float group_score(const f32x4_t (&acc)[4], const floa
   return rows4_sum(group_part(acc, wq)) * s + 0.0f;  // +0.0f: a zero score is +0
 }
 
-template <int BS>
+template <int BS, bool kFp4>
 __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ cache, int64_t num_blocks, const int32_t* __restrict__ block_table,
@@ -190,14 +242,26 @@ __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
   }
   const bool active = seq >= 0;
 
-  // A operands of this row: head 16*mt + lane%16, code bytes 32*(lane/16) .. +31
+  // A operands of this row: head 16*mt + lane%16, code bytes 32*(lane/16) .. +31.
+  // With fp4 B operands the MFMA pairs nibble j of B lane group g with A contraction
+  // slot k = 16*(g>>1) + 64*(g&1) + 32*(j>>4) + (j&15), where slot k is byte k%32 of
+  // A lane group k/32 (measured on the hardware for all 64 x 32 nibbles), and a B
+  // lane's scale byte scales its own 32 nibbles.  B lane group g holds the 32-dim
+  // scale block g (dims 32g + j), so A lane group a holds dims 16a .. 16a+15 in bytes
+  // 0..15 and 64+16a .. 64+16a+15 in bytes 16..31.
   i32x8_t qa[4];
   float wq[4][4];  // w * q_scale of the accumulator rows this lane holds
   if (active) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      qa[mt] = *reinterpret_cast<const i32x8_t*>(
-          q + ((int64_t)row * 64 + 16 * mt + (lane & 15)) * kHeadDim + 32 * (lane >> 4));
+      const uint8_t* qh = q + ((int64_t)row * 64 + 16 * mt + (lane & 15)) * kHeadDim;
+      if constexpr (kFp4) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(qh + 16 * (lane >> 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(qh + 64 + 16 * (lane >> 4));
+        qa[mt] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      } else {
+        qa[mt] = *reinterpret_cast<const i32x8_t*>(qh + 32 * (lane >> 4));
+      }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int h = 16 * mt + 4 * (lane >> 4) + v;
@@ -216,9 +280,9 @@ __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
         for (int p = k0 + lane; p < k1; p += 64) out[p] = -INFINITY;
       return;
     }
-    auto blocks = [&](int i) { return share_blocks<BS>(bt_row, k0 + i * kStageKeys, n_max, tid); };
+    auto blocks = [&](int i) { return share_blocks<BS, kFp4>(bt_row, k0 + i * kStageKeys, n_max, tid); };
     auto share = [&](const ShareBlocks& e, int i) {
-      return load_share<BS>(cache, num_blocks, e, k0 + i * kStageKeys, n_max, tid);
+      return load_share<BS, kFp4>(cache, num_blocks, e, k0 + i * kStageKeys, n_max, tid);
     };
     // Scores stage i from the staged copy st: groups of 16 keys, one 64-key store
     // per 4 groups (reads the row's operands only).
@@ -233,16 +297,29 @@ __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
       float part[4];
 #pragma unroll
       for (int g = 0; g < kStageGroups; ++g) {
-        const i32x8_t b = read_b(st, g, lane);
         f32x4_t acc[4];
+        if constexpr (kFp4) {
+          const i32x8_t b = read_b4(st, g, lane);
+          const int sb = scale_b4(reinterpret_cast<const uint32_t*>(st + kScaleOff4)[16 * g + (lane & 15)], lane);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          for (int mt = 0; mt < 4; ++mt)  // A: fp8 e4m3 at scale 2^0; B: fp4 e2m1 at its block scale
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sb);
+        } else {
+          const i32x8_t b = read_b(st, g, lane);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        }
         part[g & 3] = group_part(acc, wq);
         if ((g & 3) == 3) {  // 64 keys done: lane l gets key l of the span, one store
           const int sp = g >> 2;
-          const float sk = reinterpret_cast<const float*>(st + kScaleOff)[64 * sp + lane];
+          float sk;
+          if constexpr (kFp4)
+            sk = key_factor4(reinterpret_cast<const uint32_t*>(st + kScaleOff4)[64 * sp + lane]);
+          else
+            sk = reinterpret_cast<const float*>(st + kScaleOff)[64 * sp + lane];
           const float v0 = rows4_reduce_scatter(part[0], part[1], part[2], part[3]) * sk + 0.0f;
           const int p = p0 + 64 * sp + lane;
           const float v = p >= n ? -INFINITY : v0;  // (+0.0f above: a zero score is +0)
@@ -254,12 +331,12 @@ __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
     // the free LDS buffer, fetches stage i+3's block entries and issues stage i+2's
     // loads into the same registers, then scores stage i.
     Share r = share(blocks(0), 0);
-    store_share(stage[0], r, tid);
+    store_share<kFp4>(stage[0], r, tid);
     r = share(blocks(1), 1);
     ShareBlocks next = blocks(2);  // block entries of stage i+2 at the top of iteration i
     lds_barrier();
     for (int i = 0; i < nst; ++i) {
-      if (i + 1 < nst) store_share(stage[(i + 1) & 1], r, tid);
+      if (i + 1 < nst) store_share<kFp4>(stage[(i + 1) & 1], r, tid);
       {
         const ShareBlocks e = next;
         next = blocks(i + 3);
@@ -289,15 +366,28 @@ __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
         bad = true;
         phys = 0;
       }
-      const uint8_t* blk = cache + (int64_t)phys * (BS * 132);
       const int off = (p0 % BS) + (lane & 15);
-      const i32x8_t b = *reinterpret_cast<const i32x8_t*>(blk + off * 128 + 32 * (lane >> 4));
-      const float s = reinterpret_cast<const float*>(blk + BS * 128)[off];
       f32x4_t acc[4];
+      float s;
+      if constexpr (kFp4) {
+        const uint8_t* blk = cache + (int64_t)phys * (BS * 68);
+        const uint4 c = *reinterpret_cast<const uint4*>(blk + off * 64 + 16 * (lane >> 4));
+        const i32x8_t b = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        const int sb = scale_b4(*reinterpret_cast<const uint32_t*>(blk + BS * 64 + off * 4), lane);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sb);
+        s = 1.0f;
+      } else {
+        const uint8_t* blk = cache + (int64_t)phys * (BS * 132);
+        const i32x8_t b = *reinterpret_cast<const i32x8_t*>(blk + off * 128 + 32 * (lane >> 4));
+        s = reinterpret_cast<const float*>(blk + BS * 128)[off];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+      }
       const float sc = group_score(acc, wq, s);
       if ((lane >> 4) == g) val = sc;
     }
@@ -321,14 +411,19 @@ hipError_t launch_score_prefill(const uint8_t* q, const float* q_scale, const fl
   const int chunk_keys = (spans + kKeyChunks - 1) / kKeyChunks * kSpan;
   const int tiles = (r.rows + kWavesPf - 1) / kWavesPf;
   const dim3 grid((unsigned)(tiles * kKeyChunks)), block(kThreadsPf);
-  if (c.block_size == 64)
-    hipLaunchKernelGGL(score_prefill_kernel<64>, grid, block, 0, s, q, q_scale, w, c.base,
-                       c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq, r.row_len,
-                       r.rows, r.max_row_len, scores, ld, chunk_keys, (int)write_pad);
-  else
-    hipLaunchKernelGGL(score_prefill_kernel<32>, grid, block, 0, s, q, q_scale, w, c.base,
-                       c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq, r.row_len,
-                       r.rows, r.max_row_len, scores, ld, chunk_keys, (int)write_pad);
+#define DSA_PF_LAUNCH(BSV, FP4)                                                                     \
+  hipLaunchKernelGGL((score_prefill_kernel<BSV, FP4>), grid, block, 0, s, q, q_scale, w, c.base,     \
+                     c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq, r.row_len, \
+                     r.rows, r.max_row_len, scores, ld, chunk_keys, (int)write_pad)
+  const bool fp4 = c.dtype == 3;
+  if (c.block_size == 64) {
+    if (fp4) DSA_PF_LAUNCH(64, true);
+    else DSA_PF_LAUNCH(64, false);
+  } else {
+    if (fp4) DSA_PF_LAUNCH(32, true);
+    else DSA_PF_LAUNCH(32, false);
+  }
+#undef DSA_PF_LAUNCH
   return hipGetLastError();
 }
 

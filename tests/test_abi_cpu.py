@@ -122,7 +122,6 @@ def test_score_validation():
 
     assert call(h=32) == dsa.IDX_EUNSUPPORTED and "heads" in err(lib)
     assert call(qd=dsa.IDX_FP8_E4M3, c=cache(dtype=dsa.IDX_BF16), qs=FAKE) == dsa.IDX_EUNSUPPORTED
-    assert call(qd=dsa.IDX_FP8_E4M3, c=cache(dtype=dsa.IDX_MXFP4), qs=FAKE) == dsa.IDX_EUNSUPPORTED
     assert call(c=cache(dtype=4)) == dsa.IDX_EINVAL
     assert call(qd=dsa.IDX_FP8_E4M3) == dsa.IDX_EINVAL and "q_scale" in err(lib)
     assert call(qd=7) == dsa.IDX_EINVAL

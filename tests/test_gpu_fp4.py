@@ -2,7 +2,8 @@
 
 The store's code nibbles and e8m0 bytes are bit-exact with the oracle's quant_mxfp4
 of the same input (flags 0), and of the kernel's own pre-quantisation rows after the
-store chain; decode scoring of fp4 keys with bf16 queries matches the oracle's
+store chain; decode scoring of fp4 keys with bf16 queries, and prefill scoring with
+fp8 queries on the scaled MFMA (block scales = the e8m0 bytes), match the oracle's
 scores on the dequantised keys within the fp32-accumulation tolerance; the fused
 selection is valid under the same tolerance."""
 import numpy as np
@@ -134,11 +135,54 @@ def test_score_topk_fp4_keys():
     print(check_selection(out.cpu().numpy(), o, wl.row_len, wl.k, RTOL["fp4"]))
 
 
-def test_fp8_queries_against_fp4_keys_are_refused():
-    wl = gen.config(1, scale=0.1)
+def oracle_fp8_q(wl):
+    c, sc = O.quant_fp8(O.bf16_bits_to_f32(wl.q_bits))
+    return O.dequant_fp8(c, sc)
+
+
+@pytest.mark.parametrize("scale,bs", [(0.02, 64), (0.05, 32)])
+def test_prefill_fp8_queries_fp4_keys(scale, bs):
+    # fp8 queries (oracle-quantised from the same bf16 q) against MXFP4 keys on the
+    # scaled MFMA: the e8m0 bytes are the B block scales
+    wl = gen.config(4, scale=scale, block_size=bs)
+    assert wl.new_x_bits.shape[0] == 0
+    g = GpuWorkload(wl, key_dtype="fp4")
+    g.quantise_q()
+    out = torch.full((wl.rows, wl.max_row_len + 3), 555.0, dtype=torch.float32, device="cuda")
+    note(f"indexer_score fp8 q x MXFP4 keys rows={wl.rows} max_len={wl.max_row_len} bs={bs}")
+    dsa.indexer_score(g.q_codes, g.w, g.cache, g.rows, out, q_scale=g.q_scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[:, wl.max_row_len:] == 555.0)
+    o = oracle_scores(wl, OracleKeys(wl, "fp4"), q64=oracle_fp8_q(wl))
+    print(check_scores(got, o, wl.row_len, RTOL["fp8"]))
+
+
+def test_prefill_fp4_rows_of_different_sequences():
+    # fp8 queries on the decode layout (every row its own sequence): the per-wave
+    # direct path of the prefill kernel, with MXFP4 keys
+    wl = gen.config(3, scale=0.01)
     g = GpuWorkload(wl, key_dtype="fp4")
     g.quantise_q()
     out = torch.empty((wl.rows, wl.max_row_len), dtype=torch.float32, device="cuda")
-    with pytest.raises(dsa.IndexerError) as e:
-        dsa.indexer_score(g.q_codes, g.w, g.cache, g.rows, out, q_scale=g.q_scale)
-    assert e.value.code == dsa.IDX_EUNSUPPORTED
+    note(f"indexer_score fp8 q x MXFP4 keys, direct path rows={wl.rows}")
+    dsa.indexer_score(g.q_codes, g.w, g.cache, g.rows, out, q_scale=g.q_scale)
+    torch.cuda.synchronize()
+    o = oracle_scores(wl, OracleKeys(wl, "fp4"), q64=oracle_fp8_q(wl))
+    print(check_scores(out.cpu().numpy(), o, wl.row_len, RTOL["fp8"]))
+
+
+def test_prefill_fp4_bad_block_scores_nan():
+    wl = gen.config(4, scale=0.02)
+    bt = wl.block_table.copy()
+    bt[0, 1] = wl.num_blocks + 3
+    g = GpuWorkload(wl, key_dtype="fp4", block_table=bt)
+    g.quantise_q()
+    out = torch.empty((wl.rows, wl.max_row_len), dtype=torch.float32, device="cuda")
+    note("indexer_score fp8 q x MXFP4 keys, bad block id")
+    dsa.indexer_score(g.q_codes, g.w, g.cache, g.rows, out, q_scale=g.q_scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    bs = wl.block_size
+    assert np.all(np.isnan(got[:, bs:2 * bs]))
+    assert np.all(np.isfinite(got[:, :bs]))
