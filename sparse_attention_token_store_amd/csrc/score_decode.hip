@@ -12,10 +12,12 @@
 //    v_mfma_f32_16x16x32_bf16.  At ~8 TB/s of fp8 keys the contraction needs
 //    ~0.5 P MAC/s, far beyond the vector ALU, so it must run on the matrix cores.
 //  - Each wavefront holds the whole query row as MFMA A operands in registers
-//    (64 VGPRs) and scores its own keys: no cross-wave reduction.  The contraction
-//    index d is permuted so that lane l reads one contiguous 64-byte (bf16) or
-//    32-byte (fp8) run of key l mod 16; A uses the same permutation, so the dot
-//    products are unchanged.
+//    (64 VGPRs) and scores its own keys: no cross-wave reduction.  bf16 and fp8 keys
+//    use the plain MFMA operand order (K-step s, lane row g: dims 32*s + 8*g .. +7),
+//    so one load instruction reads 64 contiguous bytes of each of 16 query heads
+//    (or bf16 keys) rather than 16 bytes of each of 64 segments: every wave loads
+//    the whole 16 KB query row, and the scattered order had made that load, not
+//    the keys, the long pole of a short wave.
 //  - fp8 keys (score_decode_fp8_kernel) stream through a per-wave LDS ring filled by
 //    LDS DMA, which keeps two 16-key groups in flight without holding VGPRs
 //    (4 waves per SIMD).  bf16 and MXFP4 keys (score_decode_kernel) load each 64-key
@@ -87,10 +89,11 @@ __device__ __forceinline__ void load_span(SpanRaw<kKeys>& raw, uint32_t& bad, co
       if (g % 4 == 0) raw.e[g / 4] = 0;
       raw.e[g / 4] |= e8 << (8 * (g % 4));
     } else {
+      // plain MFMA order: K-step s takes dims 32*s + 8*(lane/16) .. +7
       const uint4* src = reinterpret_cast<const uint4*>(cache + ((int64_t)phys * BS + off) * 256 +
-                                                        64 * (lane >> 4));
+                                                        16 * (lane >> 4));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) raw.c[g][s] = src[s];
+      for (int s = 0; s < 4; ++s) raw.c[g][s] = src[4 * s];
     }
   }
 }
@@ -130,6 +133,25 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return x.b;
 }
 
+// A operands in the plain MFMA order: K-step s of M tile mt holds head 16*mt + lane%16,
+// dims 32*s + 8*(lane/16) .. +7, so the four lane rows of one load read 64 contiguous
+// bytes of each of 16 heads.  wv: the weights of the accumulator rows this lane
+// holds, head 16*mt + 4*(lane/16) + v.
+__device__ __forceinline__ void load_q_plain(bf16x8_t (&qa)[4][4], float (&wv)[4][4], const uint16_t* q,
+                                             const float* w, int r, int lane) {
+  const uint16_t* qr = q + (int64_t)r * 64 * kHeadDim;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + (16 * mt + (lane & 15)) * kHeadDim +
+                                                            32 * s + 8 * (lane >> 4)));
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wv[mt][v] = w[(int64_t)r * 64 + 16 * mt + 4 * (lane >> 4) + v];
+}
+
 template <int kKeys, int BS>
 __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
@@ -155,9 +177,11 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     return;
   }
 
-  // A operands: head 16*mt + lane%16, dims 32*(lane/16) + 8*s .. +7
   bf16x8_t qa[4][4];
-  {
+  float wv[4][4];
+  if constexpr (kKeys == kFp4Keys) {
+    // MXFP4: lane l keeps one whole 32-dim scale block, so K-step s of M tile mt
+    // holds head 16*mt + lane%16, dims 32*(lane/16) + 8*s .. +7
     const uint16_t* qr = q + (int64_t)r * 64 * kHeadDim;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -165,13 +189,13 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
       for (int s = 0; s < 4; ++s)
         qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(
             qr + (16 * mt + (lane & 15)) * kHeadDim + 32 * (lane >> 4) + 8 * s));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) wv[mt][v] = w[(int64_t)r * 64 + 16 * mt + 4 * (lane >> 4) + v];
+  } else {
+    load_q_plain(qa, wv, q, w, r, lane);
   }
-  // weights of the accumulator rows this lane holds: head 16*mt + 4*(lane/16) + v
-  float wv[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) wv[mt][v] = w[(int64_t)r * 64 + 16 * mt + 4 * (lane >> 4) + v];
 
   const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
 
@@ -313,28 +337,18 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
   for (int t = 0; t < kRing - 1; ++t)
     issue_group<BS>(my[t], cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
 
-  // A operands: head 16*mt + lane%16, dims 32*(lane/16) + 8*s .. +7
   bf16x8_t qa[4][4];
-  {
-    const uint16_t* qr = q + (int64_t)r * 64 * kHeadDim;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        qa[mt][s4] = as_bf16x8(*reinterpret_cast<const uint4*>(
-            qr + (16 * mt + (lane & 15)) * kHeadDim + 32 * (lane >> 4) + 8 * s4));
-  }
-  float wv[4][4];  // weights of the accumulator rows: head 16*mt + 4*(lane/16) + v
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) wv[mt][v] = w[(int64_t)r * 64 + 16 * mt + 4 * (lane >> 4) + v];
+  float wv[4][4];
+  load_q_plain(qa, wv, q, w, r, lane);
 
-  // read positions of this lane in a slot: key lane%16, chunks 2*(lane/16) and +1
+  // read positions of this lane in a slot: key lane%16, dims 32*s4 + 8*(lane/16) .. +7,
+  // i.e. half (lane/16)&1 of code chunk 2*s4 + lane/32
   const int kr = lane & 15;
   const int sw = (kr >> 1) & 7;
-  const int rd0 = kr * 128 + (((2 * (lane >> 4)) ^ sw) << 4);
-  const int rd1 = kr * 128 + (((2 * (lane >> 4) + 1) ^ sw) << 4);
+  const int g4 = lane >> 4;
+  int rd[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) rd[s4] = kr * 128 + (((2 * s4 + (g4 >> 1)) ^ sw) << 4) + 8 * (g4 & 1);
 
   float val = 0.0f;
   bool bad = false;
@@ -348,16 +362,19 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
     // because the compiler would otherwise drain every load before any LDS read
     const uint32_t sbase = (uint32_t)(uintptr_t)my[rslot];
     rslot = rslot == kRing - 1 ? 0 : rslot + 1;
-    uint4 c0, c1;
+    uint2 c[4];
     float ks;
     __asm__ volatile(
-        "s_waitcnt vmcnt(%6)\n\t"
-        "ds_read_b128 %0, %3\n\t"
-        "ds_read_b128 %1, %4\n\t"
-        "ds_read_b32 %2, %5\n\t"
+        "s_waitcnt vmcnt(%10)\n\t"
+        "ds_read_b64 %0, %5\n\t"
+        "ds_read_b64 %1, %6\n\t"
+        "ds_read_b64 %2, %7\n\t"
+        "ds_read_b64 %3, %8\n\t"
+        "ds_read_b32 %4, %9\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(c0), "=v"(c1), "=v"(ks)
-        : "v"(sbase + rd0), "v"(sbase + rd1), "v"(sbase + kGroupCodes + 4 * kr), "n"(3 * (kRing - 1))
+        : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(ks)
+        : "v"(sbase + rd[0]), "v"(sbase + rd[1]), "v"(sbase + rd[2]), "v"(sbase + rd[3]),
+          "v"(sbase + kGroupCodes + 4 * kr), "n"(3 * (kRing - 1))
         : "memory");
     const int p0 = group_pos(t);
     bad = bad || ((bad_groups >> t) & 1);
@@ -366,8 +383,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const uint4 c = (s4 >> 1) ? c1 : c0;
-      const bf16x8_t b = (s4 & 1) ? fp8x8_to_bf16x8(c.z, c.w) : fp8x8_to_bf16x8(c.x, c.y);
+      const bf16x8_t b = fp8x8_to_bf16x8(c[s4].x, c[s4].y);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s4], b, acc[mt], 0, 0, 0);
@@ -406,6 +422,9 @@ hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const R
   // aim for >= ~4 workgroups per CU on the 256-CU part, at most 8 spans per wave
   int spw = (int)(total / (4 * 1024));
   spw = spw < 1 ? 1 : (spw > 8 ? 8 : spw);
+#ifdef DSA_DECODE_SPW
+  spw = DSA_DECODE_SPW;
+#endif
   const int64_t per_wg = 4LL * spw;
   const dim3 grid((unsigned)((spans_row + per_wg - 1) / per_wg), (unsigned)r.rows), block(256);
   if constexpr (kKeys == kFp8Keys) {  // fp8 keys: the LDS-ring kernel

@@ -43,6 +43,9 @@ CASES = [
     (2, 131072, 1024, "ties"),
     (1, 200000, 2048, "heavy"),
     (2, 100000, 8192, "normal"),
+    # k <= 512 on long rows: the later levels use 4096-element chunks (R = 4)
+    (2, 131072, 512, "heavy"),
+    (3, 60000, 256, "ties"),
     (3, 1000, 1, "normal"),
     (3, 1000, 7, "ties"),
     # more live keys than the kernel's LDS list holds: the register passes
