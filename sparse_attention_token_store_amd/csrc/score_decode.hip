@@ -39,6 +39,7 @@ namespace dsa {
 namespace {
 
 constexpr int kSpan = 64;  // keys per span (one 64-token block, or two 32-token blocks)
+constexpr int kQRowBytes = 64 * kHeadDim * 2;  // one bf16 query row
 
 enum KeyKind { kBf16Keys = 0, kFp8Keys = 1, kFp4Keys = 2 };
 
@@ -133,25 +134,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return x.b;
 }
 
-// A operands in the plain MFMA order: K-step s of M tile mt holds head 16*mt + lane%16,
-// dims 32*s + 8*(lane/16) .. +7, so the four lane rows of one load read 64 contiguous
-// bytes of each of 16 heads.  wv: the weights of the accumulator rows this lane
-// holds, head 16*mt + 4*(lane/16) + v.
-__device__ __forceinline__ void load_q_plain(bf16x8_t (&qa)[4][4], float (&wv)[4][4], const uint16_t* q,
-                                             const float* w, int r, int lane) {
-  const uint16_t* qr = q + (int64_t)r * 64 * kHeadDim;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + (16 * mt + (lane & 15)) * kHeadDim +
-                                                            32 * s + 8 * (lane >> 4)));
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) wv[mt][v] = w[(int64_t)r * 64 + 16 * mt + 4 * (lane >> 4) + v];
-}
-
 template <int kKeys, int BS>
 __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
@@ -177,24 +159,47 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     return;
   }
 
+  // The query row and head weights pass through LDS once per workgroup (every wave
+  // needs all of them as operands; four copies from L2 cost more than the MFMA
+  // work).  Chunk c (16 bytes) of head h sits at c ^ (h % 16) within the head's 256
+  // bytes, so the eight lanes of a 16-byte read phase hit distinct banks.
+  __shared__ uint4 qst[kQRowBytes / 16 + 16];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(q + (int64_t)r * 64 * kHeadDim);
+    uint4 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = qrow[j * 256 + threadIdx.x];
+    float wr = 0.0f;
+    if (threadIdx.x < 64) wr = w[(int64_t)r * 64 + threadIdx.x];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = j * 256 + threadIdx.x, h = i >> 4;
+      qst[h * 16 + ((i & 15) ^ (h & 15))] = x[j];
+    }
+    if (threadIdx.x < 64) reinterpret_cast<float*>(qst + kQRowBytes / 16)[threadIdx.x] = wr;
+    lds_barrier();
+  }
+  // A operands: K-step s of M tile mt holds head 16*mt + lane%16 and, for bf16 keys,
+  // dims 32*s + 8*(lane/16) .. +7 (the plain MFMA order); for MXFP4 keys, where
+  // lane l keeps one whole 32-dim scale block of its key, dims 32*(lane/16) + 8*s ..
+  // +7.  wv: weights of the accumulator rows, head 16*mt + 4*(lane/16) + v.
   bf16x8_t qa[4][4];
   float wv[4][4];
-  if constexpr (kKeys == kFp4Keys) {
-    // MXFP4: lane l keeps one whole 32-dim scale block, so K-step s of M tile mt
-    // holds head 16*mt + lane%16, dims 32*(lane/16) + 8*s .. +7
-    const uint16_t* qr = q + (int64_t)r * 64 * kHeadDim;
+  {
+    const int hl = lane & 15, g4 = lane >> 4;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        qa[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(
-            qr + (16 * mt + (lane & 15)) * kHeadDim + 32 * (lane >> 4) + 8 * s));
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) wv[mt][v] = w[(int64_t)r * 64 + 16 * mt + 4 * (lane >> 4) + v];
-  } else {
-    load_q_plain(qa, wv, q, w, r, lane);
+      for (int s = 0; s < 4; ++s) {
+        const int c = kKeys == kFp4Keys ? 4 * g4 + s : 4 * s + g4;
+        qa[mt][s] = as_bf16x8(qst[(16 * mt + hl) * 16 + (c ^ hl)]);
+      }
+      const float4 wq = reinterpret_cast<const float4*>(qst + kQRowBytes / 16)[4 * mt + g4];
+      wv[mt][0] = wq.x;
+      wv[mt][1] = wq.y;
+      wv[mt][2] = wq.z;
+      wv[mt][3] = wq.w;
+    }
   }
 
   const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
@@ -297,7 +302,11 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
     int64_t num_blocks, const int32_t* __restrict__ block_table, int max_blocks, int num_seqs,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_len, int max_row_len,
     float* __restrict__ scores, int64_t ld, int spans_per_wave, int write_pad) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kGroupSlot];
+  // ring[slot][wave]: slot s of the four waves is contiguous, so slots 1 .. kRing-1
+  // together hold the 16 KB query row while it is staged (they are free until the
+  // wave issues its second group)
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][4][kGroupSlot];
+  static_assert((kRing - 1) * 4 * kGroupSlot >= kQRowBytes + 256, "query row and weights fit the staging slots");
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = blockIdx.y;
@@ -332,14 +341,75 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
   }
   const uint64_t bad_groups = __ballot(my_bad);
 
-  uint8_t (*my)[kGroupSlot] = ring[wave];
-#pragma unroll
-  for (int t = 0; t < kRing - 1; ++t)
-    issue_group<BS>(my[t], cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
+  auto my = [&](int slot) { return &ring[slot][wave][0]; };
 
+  // The query row goes to LDS once per workgroup (each wave copies 16 heads with LDS
+  // DMA) instead of once per wave: every wave needs all 16 KB of it as A operands,
+  // and four separate copies from L2 had cost more than all the MFMA work.  Chunk c
+  // (16 bytes) of head h sits at position c ^ (h % 16) of the head's 256 bytes, so
+  // the eight lanes of a 16-byte read phase (eight heads, one chunk) hit distinct
+  // banks.  The copy is issued before group 0, so waiting for it leaves group 0 in
+  // flight.
+  // The head weights (256 bytes) follow the query row in the staging slots, copied
+  // by wave 0.  (Loaded into registers directly, they would be the only loads the
+  // compiler tracks, and it would wait for every load, the key groups included,
+  // before the first group.)
+  uint8_t* qs = &ring[1][0][0];
+  {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q) + (int64_t)r * 64 * kHeadDim * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int P = (wave * 4 + j) * 1024 + lane * 16, h = P >> 8;
+      const int c = ((P >> 4) & 15) ^ (h & 15);
+      __builtin_amdgcn_global_load_lds(qrow + h * 256 + c * 16, (lds_void*)(qs + (wave * 4 + j) * 1024), 16, 0, 0);
+    }
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds(w + (int64_t)r * 64 + lane, (lds_void*)(qs + kQRowBytes), 4, 0, 0);
+  }
+  issue_group<BS>(my(0), cache, __builtin_amdgcn_readlane(my_phys, 0), group_pos(0), lane);
+  __asm__ volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");  // every wave's share landed
+
+  // A operands in the plain MFMA order: K-step s4 of M tile mt holds head
+  // 16*mt + lane%16, dims 32*s4 + 8*(lane/16) .. +7 (chunk 4*s4 + lane/16)
+  // wv: weights of the accumulator rows this lane holds, head 16*mt + 4*(lane/16) + v
   bf16x8_t qa[4][4];
   float wv[4][4];
-  load_q_plain(qa, wv, q, w, r, lane);
+  {
+    const uint32_t qb = (uint32_t)(uintptr_t)qs;
+    const int hl = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint32_t hb = qb + (16 * mt + hl) * 256;
+      uint4 x0, x1, x2, x3;
+      float4 wq;
+      __asm__ volatile(
+          "ds_read_b128 %0, %5\n\t"
+          "ds_read_b128 %1, %6\n\t"
+          "ds_read_b128 %2, %7\n\t"
+          "ds_read_b128 %3, %8\n\t"
+          "ds_read_b128 %4, %9\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(wq)
+          : "v"(hb + (((0 + g4) ^ hl) << 4)), "v"(hb + (((4 + g4) ^ hl) << 4)),
+            "v"(hb + (((8 + g4) ^ hl) << 4)), "v"(hb + (((12 + g4) ^ hl) << 4)),
+            "v"(qb + kQRowBytes + (16 * mt + 4 * g4) * 4)
+          : "memory");
+      qa[mt][0] = as_bf16x8(x0);
+      qa[mt][1] = as_bf16x8(x1);
+      qa[mt][2] = as_bf16x8(x2);
+      qa[mt][3] = as_bf16x8(x3);
+      wv[mt][0] = wq.x;
+      wv[mt][1] = wq.y;
+      wv[mt][2] = wq.z;
+      wv[mt][3] = wq.w;
+    }
+  }
+  __asm__ volatile("s_barrier" ::: "memory");  // every wave has its operands: the slots are free
+#pragma unroll
+  for (int t = 1; t < kRing - 1; ++t)
+    issue_group<BS>(my(t), cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
+
 
   // read positions of this lane in a slot: key lane%16, dims 32*s4 + 8*(lane/16) .. +7,
   // i.e. half (lane/16)&1 of code chunk 2*s4 + lane/32
@@ -355,12 +425,12 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
   int wslot = kRing - 1, rslot = 0;
   for (int t = 0; t < ngroups; ++t) {
     const int tn = t + kRing - 1;  // (readlane of a lane >= ngroups gives block 0)
-    issue_group<BS>(my[wslot], cache, __builtin_amdgcn_readlane(my_phys, tn & 63), group_pos(tn), lane);
+    issue_group<BS>(my(wslot), cache, __builtin_amdgcn_readlane(my_phys, tn & 63), group_pos(tn), lane);
     wslot = wslot == kRing - 1 ? 0 : wslot + 1;
     // wait for group t (3 loads x (kRing - 1) newer groups may stay in flight), then
     // read this lane's two code chunks and its key's scale; the waits sit in the asm
     // because the compiler would otherwise drain every load before any LDS read
-    const uint32_t sbase = (uint32_t)(uintptr_t)my[rslot];
+    const uint32_t sbase = (uint32_t)(uintptr_t)my(rslot);
     rslot = rslot == kRing - 1 ? 0 : rslot + 1;
     uint2 c[4];
     float ks;
