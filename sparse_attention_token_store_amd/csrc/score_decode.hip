@@ -12,16 +12,15 @@
 //    v_mfma_f32_16x16x32_bf16.  At ~8 TB/s of fp8 keys the contraction needs
 //    ~0.5 P MAC/s, far beyond the vector ALU, so it must run on the matrix cores.
 //  - Each wavefront holds the whole query row as MFMA A operands in registers
-//    (64 VGPRs) and scores its own keys: no cross-wave reduction.  bf16 and fp8 keys
-//    use the plain MFMA operand order (K-step s, lane row g: dims 32*s + 8*g .. +7),
-//    so one load instruction reads 64 contiguous bytes of each of 16 query heads
-//    (or bf16 keys) rather than 16 bytes of each of 64 segments: every wave loads
-//    the whole 16 KB query row, and the scattered order had made that load, not
-//    the keys, the long pole of a short wave.
-//  - fp8 keys (score_decode_fp8_kernel) stream through a per-wave LDS ring filled by
-//    LDS DMA, which keeps two 16-key groups in flight without holding VGPRs
-//    (4 waves per SIMD).  bf16 and MXFP4 keys (score_decode_kernel) load each 64-key
-//    span straight into registers with the next span prefetched.
+//    (64 VGPRs) and scores its own keys: no cross-wave reduction.  The row (16 KB)
+//    is copied into LDS once per workgroup and read from there by every wave.  bf16
+//    and fp8 keys use the plain MFMA operand order (K-step s, lane row g: dims
+//    32*s + 8*g .. +7), so one load instruction reads 64 contiguous bytes of each of
+//    16 bf16 keys.
+//  - fp8 and MXFP4 keys (score_decode_ring_kernel) stream through a per-wave LDS
+//    ring filled by LDS DMA, which keeps several 16-key groups in flight without
+//    holding VGPRs (4 waves per SIMD).  bf16 keys (score_decode_bf16_kernel) load
+//    each 64-key span straight into registers with the next span prefetched.
 //  - fp8 codes are widened to bf16 exactly (every e4m3 value is a bf16 value) with
 //    v_cvt_scalef32_pk_bf16_fp8; the per-key scale multiplies the head sum.
 //  - MXFP4: lane l's 32 contiguous dims 32*(l/16) .. +31 are exactly one 32-element
@@ -43,38 +42,22 @@ constexpr int kQRowBytes = 64 * kHeadDim * 2;  // one bf16 query row
 
 enum KeyKind { kBf16Keys = 0, kFp8Keys = 1, kFp4Keys = 2 };
 
-// Keys per wave span of the register kernel (a multiple of 64).  MXFP4 keys use
-// 64-key spans too: measured on 16 x 131072 keys, 128- and 192-key spans (more bytes
-// in flight, more VGPRs) were 6% and 16% slower; the kernel is bound by the per-group
-// widening and MFMA work at 2 waves per SIMD, not by loads in flight.
-#ifndef DSA_FP4_SPAN
-#define DSA_FP4_SPAN 64
-#endif
-template <int kKeys>
-constexpr int span_keys() { return kKeys == kFp4Keys ? DSA_FP4_SPAN : 64; }
-
-template <int kKeys>
-struct SpanRaw;
-template <>
-struct SpanRaw<kBf16Keys> {
-  uint4 c[4][4];  // per 16-key group: 64 bytes (32 bf16) of this lane's key
-};
-template <>
-struct SpanRaw<kFp4Keys> {
-  uint4 c[DSA_FP4_SPAN / 16];     // per 16-key group: 16 code bytes (32 e2m1) of this lane's key
-  uint32_t e[DSA_FP4_SPAN / 64];  // per group g: e8m0 byte of this lane's block, byte g % 4
+// One wave span of bf16 keys in registers: per 16-key group, 64 bytes (32 bf16) of
+// this lane's key.
+struct SpanRaw {
+  uint4 c[4][4];
 };
 
 // Loads the keys of one span for this lane.  Groups at or past the row's length are
 // not touched (their block-table entries may not exist); a block id outside the pool
 // sets the group's bit in `bad` and reads block 0 instead.
-template <int kKeys, int BS>
-__device__ __forceinline__ void load_span(SpanRaw<kKeys>& raw, uint32_t& bad, const uint8_t* cache,
+template <int BS>
+__device__ __forceinline__ void load_span(SpanRaw& raw, uint32_t& bad, const uint8_t* cache,
                                           int64_t num_blocks, const int32_t* bt_row, int p_span,
                                           int n, int lane) {
   bad = 0;
 #pragma unroll
-  for (int g = 0; g < span_keys<kKeys>() / 16; ++g) {
+  for (int g = 0; g < kSpan / 16; ++g) {
     const int p0 = p_span + 16 * g;
     if (p0 >= n) continue;  // uniform per wave
     int phys = bt_row[p0 / BS];
@@ -83,19 +66,11 @@ __device__ __forceinline__ void load_span(SpanRaw<kKeys>& raw, uint32_t& bad, co
       phys = 0;
     }
     const int off = (p0 % BS) + (lane & 15);
-    if constexpr (kKeys == kFp4Keys) {
-      const uint8_t* blk = cache + (int64_t)phys * (BS * 68);
-      raw.c[g] = *reinterpret_cast<const uint4*>(blk + off * 64 + 16 * (lane >> 4));
-      const uint32_t e8 = blk[BS * 64 + off * 4 + (lane >> 4)];
-      if (g % 4 == 0) raw.e[g / 4] = 0;
-      raw.e[g / 4] |= e8 << (8 * (g % 4));
-    } else {
-      // plain MFMA order: K-step s takes dims 32*s + 8*(lane/16) .. +7
-      const uint4* src = reinterpret_cast<const uint4*>(cache + ((int64_t)phys * BS + off) * 256 +
-                                                        16 * (lane >> 4));
+    // plain MFMA order: K-step s takes dims 32*s + 8*(lane/16) .. +7
+    const uint4* src = reinterpret_cast<const uint4*>(cache + ((int64_t)phys * BS + off) * 256 +
+                                                      16 * (lane >> 4));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) raw.c[g][s] = src[4 * s];
-    }
+    for (int s = 0; s < 4; ++s) raw.c[g][s] = src[4 * s];
   }
 }
 
@@ -134,8 +109,8 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return x.b;
 }
 
-template <int kKeys, int BS>
-__global__ __launch_bounds__(256, 2) void score_decode_kernel(
+template <int BS>
+__global__ __launch_bounds__(256, 2) void score_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
     int64_t num_blocks, const int32_t* __restrict__ block_table, int max_blocks, int num_seqs,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_len, int max_row_len,
@@ -146,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
   const int seq = row_seq[r];
   const int n = min(max(row_len[r], 0), max_row_len);
   float* out = scores + (int64_t)r * ld;
-  constexpr int KS = span_keys<kKeys>();
+  constexpr int KS = kSpan;
   const int chunk0 = blockIdx.x * (4 * spans_per_wave * KS);
   const bool seq_bad = seq < 0 || seq >= num_seqs;
 
@@ -179,10 +154,9 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     if (threadIdx.x < 64) reinterpret_cast<float*>(qst + kQRowBytes / 16)[threadIdx.x] = wr;
     lds_barrier();
   }
-  // A operands: K-step s of M tile mt holds head 16*mt + lane%16 and, for bf16 keys,
-  // dims 32*s + 8*(lane/16) .. +7 (the plain MFMA order); for MXFP4 keys, where
-  // lane l keeps one whole 32-dim scale block of its key, dims 32*(lane/16) + 8*s ..
-  // +7.  wv: weights of the accumulator rows, head 16*mt + 4*(lane/16) + v.
+  // A operands in the plain MFMA order: K-step s of M tile mt holds head
+  // 16*mt + lane%16, dims 32*s + 8*(lane/16) .. +7 (chunk 4*s + lane/16).  wv: weights
+  // of the accumulator rows, head 16*mt + 4*(lane/16) + v.
   bf16x8_t qa[4][4];
   float wv[4][4];
   {
@@ -191,8 +165,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int c = kKeys == kFp4Keys ? 4 * g4 + s : 4 * s + g4;
-        qa[mt][s] = as_bf16x8(qst[(16 * mt + hl) * 16 + (c ^ hl)]);
+        qa[mt][s] = as_bf16x8(qst[(16 * mt + hl) * 16 + ((4 * s + g4) ^ hl)]);
       }
       const float4 wq = reinterpret_cast<const float4*>(qst + kQRowBytes / 16)[4 * mt + g4];
       wv[mt][0] = wq.x;
@@ -204,15 +177,15 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
 
   const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
 
-  SpanRaw<kKeys> cur, nxt;
+  SpanRaw cur, nxt;
   uint32_t cur_bad = 0, nxt_bad = 0;
   int p_span = chunk0 + wave * KS;
-  if (p_span < n) load_span<kKeys, BS>(cur, cur_bad, cache, num_blocks, bt_row, p_span, n, lane);
+  if (p_span < n) load_span<BS>(cur, cur_bad, cache, num_blocks, bt_row, p_span, n, lane);
 
   for (int i = 0; i < spans_per_wave; ++i, p_span += 4 * KS) {
     const int p_next = p_span + 4 * KS;
     if (i + 1 < spans_per_wave && p_next < n)
-      load_span<kKeys, BS>(nxt, nxt_bad, cache, num_blocks, bt_row, p_next, n, lane);
+      load_span<BS>(nxt, nxt_bad, cache, num_blocks, bt_row, p_next, n, lane);
 
     if (p_span < n) {
 #pragma unroll
@@ -226,15 +199,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
           for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            bf16x8_t b;
-            if constexpr (kKeys == kFp4Keys) {
-              const uint4 c = cur.c[gg];
-              const uint32_t d = s == 0 ? c.x : (s == 1 ? c.y : (s == 2 ? c.z : c.w));
-              const uint32_t e8 = (cur.e[gg / 4] >> (8 * (gg % 4))) & 0xFFu;
-              b = fp4x8_to_bf16x8(d, __uint_as_float(e8 ? e8 << 23 : 0x00400000u));  // 2^(e8-127)
-            } else {
-              b = as_bf16x8(cur.c[gg][s]);
-            }
+            const bf16x8_t b = as_bf16x8(cur.c[gg][s]);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
               acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], b, acc[mt], 0, 0, 0);
@@ -265,39 +230,62 @@ __global__ __launch_bounds__(256, 2) void score_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// fp8 keys: the same tiling, with the key stream moved to LDS DMA.  Each wave owns
-// a ring of kRing 16-key group slots in LDS and keeps kRing-1 groups in flight with
-// global_load_lds (no VGPRs held by loads in flight), so far more bytes are
-// outstanding per wave than a register double buffer allows at 2 waves per SIMD.
-// Every group issues exactly 3 loads (2 x 1 KB of codes, 64 B of scales), so a
-// fixed vmcnt wait guarantees the group about to be read has landed; the score
-// stores interleaved with the loads only make that wait stricter.  Within a slot,
-// code chunk c of key r sits at position r*8 + (c ^ ((r >> 1) & 7)): the 16 lanes
-// of a 16-byte read phase (16 keys, same chunk) then hit 16 distinct bank groups.
+// fp8 and MXFP4 keys: the same tiling, with the key stream moved to LDS DMA.  Each
+// wave owns a ring of kRing 16-key group slots in LDS and keeps kRing-1 groups in
+// flight with global_load_lds (no VGPRs held by loads in flight), so far more bytes
+// are outstanding per wave than a register double buffer allows at 2 waves per SIMD.
+// Every group issues a fixed number of loads (fp8: 2 x 1 KB of codes and 64 B of
+// scales; MXFP4: 1 KB of codes and 64 B of e8m0 scales), so a fixed vmcnt wait
+// guarantees the group about to be read has landed; the score stores interleaved
+// with the loads only make that wait stricter.  Within a slot, 16-byte code chunks
+// are XOR-swizzled by key so a read phase (several keys, same chunk) hits distinct
+// banks: fp8 chunk c of key r sits at position r*8 + (c ^ ((r >> 1) & 7)), MXFP4
+// chunk c at r*4 + (c ^ ((r >> 2) & 3)).
 constexpr int kGroupCodes = 16 * 128;
 constexpr int kGroupSlot = kGroupCodes + 16 * 4;  // 2112 bytes
+constexpr int kGroupCodes4 = 16 * 64;
+constexpr int kGroupSlot4 = kGroupCodes4 + 16 * 4;  // 1088 bytes
 #ifndef DSA_DECODE_RING
 #define DSA_DECODE_RING 3
 #endif
-constexpr int kDecodeRing = DSA_DECODE_RING;  // LDS slots per wave
+#ifndef DSA_DECODE_RING4
+#define DSA_DECODE_RING4 6
+#endif
+constexpr int kDecodeRing = DSA_DECODE_RING;    // LDS slots per wave, fp8 keys
+constexpr int kDecodeRing4 = DSA_DECODE_RING4;  // MXFP4 keys (smaller slots, deeper ring)
 
-template <int BS>
+template <bool kFp4>
+struct RingKeys {
+  static constexpr int kCodes = kFp4 ? kGroupCodes4 : kGroupCodes;  // code bytes of a group
+  static constexpr int kSlot = kFp4 ? kGroupSlot4 : kGroupSlot;
+  static constexpr int kKeyBytes = kFp4 ? 68 : 132;  // cache bytes per token
+  static constexpr int kLoads = kFp4 ? 2 : 3;        // load instructions per group
+};
+
+template <int BS, bool kFp4>
 __device__ __forceinline__ void issue_group(uint8_t* slot, const uint8_t* cache, int phys, int p0, int lane) {
   typedef __attribute__((address_space(3))) void lds_void;
-  const uint8_t* blk = cache + (int64_t)phys * (BS * 132);
+  constexpr int kCodeRow = kFp4 ? 64 : 128;  // code bytes per key
+  const uint8_t* blk = cache + (int64_t)phys * (BS * RingKeys<kFp4>::kKeyBytes);
   const int off = p0 % BS;
+  if constexpr (kFp4) {
+    const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+    __builtin_amdgcn_global_load_lds(blk + (off + r) * 64 + c * 16, (lds_void*)slot, 16, 0, 0);
+  } else {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int sidx = j * 64 + lane, r = sidx >> 3, c = (sidx & 7) ^ ((r >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(blk + (off + r) * 128 + c * 16,
-                                     (lds_void*)(slot + j * 1024), 16, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      const int sidx = j * 64 + lane, r = sidx >> 3, c = (sidx & 7) ^ ((r >> 1) & 7);
+      __builtin_amdgcn_global_load_lds(blk + (off + r) * 128 + c * 16,
+                                       (lds_void*)(slot + j * 1024), 16, 0, 0);
+    }
   }
-  if (lane < 16)
-    __builtin_amdgcn_global_load_lds(blk + BS * 128 + (off + lane) * 4, (lds_void*)(slot + kGroupCodes), 4, 0, 0);
+  if (lane < 16)  // the 16 keys' scale words (fp32, or four e8m0 bytes)
+    __builtin_amdgcn_global_load_lds(blk + BS * kCodeRow + (off + lane) * 4,
+                                     (lds_void*)(slot + RingKeys<kFp4>::kCodes), 4, 0, 0);
 }
 
-template <int BS, int kRing>
-__global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
+template <int BS, int kRing, bool kFp4>
+__global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
     int64_t num_blocks, const int32_t* __restrict__ block_table, int max_blocks, int num_seqs,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_len, int max_row_len,
@@ -305,8 +293,9 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
   // ring[slot][wave]: slot s of the four waves is contiguous, so slots 1 .. kRing-1
   // together hold the 16 KB query row while it is staged (they are free until the
   // wave issues its second group)
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][4][kGroupSlot];
-  static_assert((kRing - 1) * 4 * kGroupSlot >= kQRowBytes + 256, "query row and weights fit the staging slots");
+  constexpr int kSlot = RingKeys<kFp4>::kSlot;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][4][kSlot];
+  static_assert((kRing - 1) * 4 * kSlot >= kQRowBytes + 256, "query row and weights fit the staging slots");
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = blockIdx.y;
@@ -367,17 +356,21 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
     if (wave == 0)
       __builtin_amdgcn_global_load_lds(w + (int64_t)r * 64 + lane, (lds_void*)(qs + kQRowBytes), 4, 0, 0);
   }
-  issue_group<BS>(my(0), cache, __builtin_amdgcn_readlane(my_phys, 0), group_pos(0), lane);
-  __asm__ volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");  // every wave's share landed
+  issue_group<BS, kFp4>(my(0), cache, __builtin_amdgcn_readlane(my_phys, 0), group_pos(0), lane);
+  // every wave's share landed (group 0's loads may stay in flight)
+  __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(RingKeys<kFp4>::kLoads) : "memory");
 
-  // A operands in the plain MFMA order: K-step s4 of M tile mt holds head
-  // 16*mt + lane%16, dims 32*s4 + 8*(lane/16) .. +7 (chunk 4*s4 + lane/16)
+  // A operands: K-step s4 of M tile mt holds head 16*mt + lane%16 and, for fp8 keys,
+  // dims 32*s4 + 8*(lane/16) .. +7 (chunk 4*s4 + lane/16, the plain MFMA order); for
+  // MXFP4 keys, whose lane keeps one whole 32-dim scale block, dims 32*(lane/16) +
+  // 8*s4 .. +7 (chunk 4*(lane/16) + s4)
   // wv: weights of the accumulator rows this lane holds, head 16*mt + 4*(lane/16) + v
   bf16x8_t qa[4][4];
   float wv[4][4];
   {
     const uint32_t qb = (uint32_t)(uintptr_t)qs;
     const int hl = lane & 15, g4 = lane >> 4;
+    auto qchunk = [&](int s4) { return kFp4 ? 4 * g4 + s4 : 4 * s4 + g4; };
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const uint32_t hb = qb + (16 * mt + hl) * 256;
@@ -391,8 +384,8 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
           "ds_read_b128 %4, %9\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(wq)
-          : "v"(hb + (((0 + g4) ^ hl) << 4)), "v"(hb + (((4 + g4) ^ hl) << 4)),
-            "v"(hb + (((8 + g4) ^ hl) << 4)), "v"(hb + (((12 + g4) ^ hl) << 4)),
+          : "v"(hb + ((qchunk(0) ^ hl) << 4)), "v"(hb + ((qchunk(1) ^ hl) << 4)),
+            "v"(hb + ((qchunk(2) ^ hl) << 4)), "v"(hb + ((qchunk(3) ^ hl) << 4)),
             "v"(qb + kQRowBytes + (16 * mt + 4 * g4) * 4)
           : "memory");
       qa[mt][0] = as_bf16x8(x0);
@@ -408,44 +401,73 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
   __asm__ volatile("s_barrier" ::: "memory");  // every wave has its operands: the slots are free
 #pragma unroll
   for (int t = 1; t < kRing - 1; ++t)
-    issue_group<BS>(my(t), cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
+    issue_group<BS, kFp4>(my(t), cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
 
 
-  // read positions of this lane in a slot: key lane%16, dims 32*s4 + 8*(lane/16) .. +7,
-  // i.e. half (lane/16)&1 of code chunk 2*s4 + lane/32
+  // read positions of this lane in a slot: key lane%16; fp8: dims 32*s4 + 8*(lane/16)
+  // .. +7, i.e. half (lane/16)&1 of code chunk 2*s4 + lane/32; MXFP4: code chunk
+  // lane/16 (dims 32*(lane/16) .. +31) and scale byte lane/16 of the key's word
   const int kr = lane & 15;
-  const int sw = (kr >> 1) & 7;
   const int g4 = lane >> 4;
   int rd[4];
+  if constexpr (kFp4) {
+    rd[0] = kr * 64 + ((g4 ^ ((kr >> 2) & 3)) << 4);
+    rd[1] = rd[2] = rd[3] = rd[0];
+  } else {
+    const int sw = (kr >> 1) & 7;
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) rd[s4] = kr * 128 + (((2 * s4 + (g4 >> 1)) ^ sw) << 4) + 8 * (g4 & 1);
+    for (int s4 = 0; s4 < 4; ++s4) rd[s4] = kr * 128 + (((2 * s4 + (g4 >> 1)) ^ sw) << 4) + 8 * (g4 & 1);
+  }
 
   float val = 0.0f;
   bool bad = false;
   int wslot = kRing - 1, rslot = 0;
   for (int t = 0; t < ngroups; ++t) {
     const int tn = t + kRing - 1;  // (readlane of a lane >= ngroups gives block 0)
-    issue_group<BS>(my(wslot), cache, __builtin_amdgcn_readlane(my_phys, tn & 63), group_pos(tn), lane);
+    issue_group<BS, kFp4>(my(wslot), cache, __builtin_amdgcn_readlane(my_phys, tn & 63), group_pos(tn), lane);
     wslot = wslot == kRing - 1 ? 0 : wslot + 1;
     // wait for group t (3 loads x (kRing - 1) newer groups may stay in flight), then
     // read this lane's two code chunks and its key's scale; the waits sit in the asm
     // because the compiler would otherwise drain every load before any LDS read
     const uint32_t sbase = (uint32_t)(uintptr_t)my(rslot);
     rslot = rslot == kRing - 1 ? 0 : rslot + 1;
+    // the slot's codes: fp8, four 8-byte halves (one per K-step); MXFP4, one 16-byte
+    // chunk (one dword per K-step) and the key's four e8m0 bytes
     uint2 c[4];
-    float ks;
-    __asm__ volatile(
-        "s_waitcnt vmcnt(%10)\n\t"
-        "ds_read_b64 %0, %5\n\t"
-        "ds_read_b64 %1, %6\n\t"
-        "ds_read_b64 %2, %7\n\t"
-        "ds_read_b64 %3, %8\n\t"
-        "ds_read_b32 %4, %9\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(ks)
-        : "v"(sbase + rd[0]), "v"(sbase + rd[1]), "v"(sbase + rd[2]), "v"(sbase + rd[3]),
-          "v"(sbase + kGroupCodes + 4 * kr), "n"(3 * (kRing - 1))
-        : "memory");
+    float ks;  // the key's scale (fp8), or 1 (MXFP4: the block scale is in the B operand)
+    float bscale = 1.0f;
+    if constexpr (kFp4) {
+      uint4 c4;
+      uint32_t sw4;
+      __asm__ volatile(
+          "s_waitcnt vmcnt(%4)\n\t"
+          "ds_read_b128 %0, %2\n\t"
+          "ds_read_b32 %1, %3\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(c4), "=&v"(sw4)
+          : "v"(sbase + rd[0]), "v"(sbase + kGroupCodes4 + 4 * kr), "n"(2 * (kRing - 1))
+          : "memory");
+      const uint32_t e8 = (sw4 >> (8 * g4)) & 0xFFu;
+      bscale = __uint_as_float(e8 ? e8 << 23 : 0x00400000u);  // 2^(e8-127)
+      c[0].x = c4.x;
+      c[1].x = c4.y;
+      c[2].x = c4.z;
+      c[3].x = c4.w;
+      ks = 1.0f;
+    } else {
+      __asm__ volatile(
+          "s_waitcnt vmcnt(%10)\n\t"
+          "ds_read_b64 %0, %5\n\t"
+          "ds_read_b64 %1, %6\n\t"
+          "ds_read_b64 %2, %7\n\t"
+          "ds_read_b64 %3, %8\n\t"
+          "ds_read_b32 %4, %9\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(ks)
+          : "v"(sbase + rd[0]), "v"(sbase + rd[1]), "v"(sbase + rd[2]), "v"(sbase + rd[3]),
+            "v"(sbase + kGroupCodes + 4 * kr), "n"(3 * (kRing - 1))
+          : "memory");
+    }
     const int p0 = group_pos(t);
     bad = bad || ((bad_groups >> t) & 1);
     f32x4_t acc[4];
@@ -453,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const bf16x8_t b = fp8x8_to_bf16x8(c[s4].x, c[s4].y);
+      const bf16x8_t b = kFp4 ? fp4x8_to_bf16x8(c[s4].x, bscale) : fp8x8_to_bf16x8(c[s4].x, c[s4].y);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s4], b, acc[mt], 0, 0, 0);
@@ -486,8 +508,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_fp8_kernel(
 template <int kKeys>
 hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const Rows& r,
                      float* scores, int64_t ld, bool write_pad, hipStream_t s) {
-  constexpr int KS = kKeys == kFp8Keys ? kSpan : span_keys<kKeys>();
-  const int64_t spans_row = (r.max_row_len + KS - 1) / KS;
+  const int64_t spans_row = (r.max_row_len + kSpan - 1) / kSpan;
   const int64_t total = spans_row * r.rows;
   // aim for >= ~4 workgroups per CU on the 256-CU part, at most 8 spans per wave
   int spw = (int)(total / (4 * 1024));
@@ -497,25 +518,27 @@ hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const R
 #endif
   const int64_t per_wg = 4LL * spw;
   const dim3 grid((unsigned)((spans_row + per_wg - 1) / per_wg), (unsigned)r.rows), block(256);
+#define DSA_RING_LAUNCH(BSV, RING, FP4)                                                              \
+  hipLaunchKernelGGL((score_decode_ring_kernel<BSV, RING, FP4>), grid, block, 0, s, q, w, c.base,   \
+                     c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq, r.row_len, \
+                     r.max_row_len, scores, ld, spw, (int)write_pad)
   if constexpr (kKeys == kFp8Keys) {  // fp8 keys: the LDS-ring kernel
+    if (c.block_size == 64) DSA_RING_LAUNCH(64, kDecodeRing, false);
+    else DSA_RING_LAUNCH(32, kDecodeRing, false);
+  } else if constexpr (kKeys == kFp4Keys) {  // MXFP4 keys: the LDS-ring kernel
+    if (c.block_size == 64) DSA_RING_LAUNCH(64, kDecodeRing4, true);
+    else DSA_RING_LAUNCH(32, kDecodeRing4, true);
+  } else {  // bf16 keys: the register-streaming kernel
     if (c.block_size == 64)
-      hipLaunchKernelGGL((score_decode_fp8_kernel<64, kDecodeRing>), grid, block, 0, s, q, w, c.base,
+      hipLaunchKernelGGL((score_decode_bf16_kernel<64>), grid, block, 0, s, q, w, c.base,
                          c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
                          r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
     else
-      hipLaunchKernelGGL((score_decode_fp8_kernel<32, kDecodeRing>), grid, block, 0, s, q, w, c.base,
-                         c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
-                         r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
-  } else {  // bf16 or MXFP4 keys: the register-streaming kernel
-    if (c.block_size == 64)
-      hipLaunchKernelGGL((score_decode_kernel<kKeys, 64>), grid, block, 0, s, q, w, c.base,
-                         c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
-                         r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
-    else
-      hipLaunchKernelGGL((score_decode_kernel<kKeys, 32>), grid, block, 0, s, q, w, c.base,
+      hipLaunchKernelGGL((score_decode_bf16_kernel<32>), grid, block, 0, s, q, w, c.base,
                          c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
                          r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
   }
+#undef DSA_RING_LAUNCH
   return hipGetLastError();
 }
 
