@@ -262,26 +262,31 @@ struct RingKeys {
   static constexpr int kLoads = kFp4 ? 2 : 3;        // load instructions per group
 };
 
+// Every key group is read once.  fp8 groups are loaded with the non-temporal cache
+// policy (NT), which leaves L2 to the query rows and block tables: measured 8%
+// faster on decode batch 32 and 4% on 16 x 128k keys.  MXFP4 groups, at half the
+// bytes, measured no gain and keep the default policy.
 template <int BS, bool kFp4>
 __device__ __forceinline__ void issue_group(uint8_t* slot, const uint8_t* cache, int phys, int p0, int lane) {
   typedef __attribute__((address_space(3))) void lds_void;
   constexpr int kCodeRow = kFp4 ? 64 : 128;  // code bytes per key
+  constexpr int kCpol = kFp4 ? 0 : 2;        // cache policy bits of the loads: 2 = NT
   const uint8_t* blk = cache + (int64_t)phys * (BS * RingKeys<kFp4>::kKeyBytes);
   const int off = p0 % BS;
   if constexpr (kFp4) {
     const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
-    __builtin_amdgcn_global_load_lds(blk + (off + r) * 64 + c * 16, (lds_void*)slot, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(blk + (off + r) * 64 + c * 16, (lds_void*)slot, 16, 0, kCpol);
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int sidx = j * 64 + lane, r = sidx >> 3, c = (sidx & 7) ^ ((r >> 1) & 7);
       __builtin_amdgcn_global_load_lds(blk + (off + r) * 128 + c * 16,
-                                       (lds_void*)(slot + j * 1024), 16, 0, 0);
+                                       (lds_void*)(slot + j * 1024), 16, 0, kCpol);
     }
   }
   if (lane < 16)  // the 16 keys' scale words (fp32, or four e8m0 bytes)
     __builtin_amdgcn_global_load_lds(blk + BS * kCodeRow + (off + lane) * 4,
-                                     (lds_void*)(slot + RingKeys<kFp4>::kCodes), 4, 0, 0);
+                                     (lds_void*)(slot + RingKeys<kFp4>::kCodes), 4, 0, kCpol);
 }
 
 template <int BS, int kRing, bool kFp4>
