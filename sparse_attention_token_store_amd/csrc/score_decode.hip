@@ -15,12 +15,10 @@
 //    (64 VGPRs) and scores its own keys: no cross-wave reduction.  The row (16 KB)
 //    is copied into LDS once per workgroup and read from there by every wave.  bf16
 //    and fp8 keys use the plain MFMA operand order (K-step s, lane row g: dims
-//    32*s + 8*g .. +7), so one load instruction reads 64 contiguous bytes of each of
-//    16 bf16 keys.
-//  - fp8 and MXFP4 keys (score_decode_ring_kernel) stream through a per-wave LDS
-//    ring filled by LDS DMA, which keeps several 16-key groups in flight without
-//    holding VGPRs (4 waves per SIMD).  bf16 keys (score_decode_bf16_kernel) load
-//    each 64-key span straight into registers with the next span prefetched.
+//    32*s + 8*g .. +7).
+//  - Keys of every format stream through a per-wave LDS ring filled by LDS DMA
+//    (score_decode_ring_kernel), which keeps several 16-key groups in flight
+//    without holding VGPRs.
 //  - fp8 codes are widened to bf16 exactly (every e4m3 value is a bf16 value) with
 //    v_cvt_scalef32_pk_bf16_fp8; the per-key scale multiplies the head sum.
 //  - MXFP4: lane l's 32 contiguous dims 32*(l/16) .. +31 are exactly one 32-element
@@ -41,38 +39,6 @@ constexpr int kSpan = 64;  // keys per span (one 64-token block, or two 32-token
 constexpr int kQRowBytes = 64 * kHeadDim * 2;  // one bf16 query row
 
 enum KeyKind { kBf16Keys = 0, kFp8Keys = 1, kFp4Keys = 2 };
-
-// One wave span of bf16 keys in registers: per 16-key group, 64 bytes (32 bf16) of
-// this lane's key.
-struct SpanRaw {
-  uint4 c[4][4];
-};
-
-// Loads the keys of one span for this lane.  Groups at or past the row's length are
-// not touched (their block-table entries may not exist); a block id outside the pool
-// sets the group's bit in `bad` and reads block 0 instead.
-template <int BS>
-__device__ __forceinline__ void load_span(SpanRaw& raw, uint32_t& bad, const uint8_t* cache,
-                                          int64_t num_blocks, const int32_t* bt_row, int p_span,
-                                          int n, int lane) {
-  bad = 0;
-#pragma unroll
-  for (int g = 0; g < kSpan / 16; ++g) {
-    const int p0 = p_span + 16 * g;
-    if (p0 >= n) continue;  // uniform per wave
-    int phys = bt_row[p0 / BS];
-    if (phys < 0 || phys >= num_blocks) {
-      bad |= 1u << g;
-      phys = 0;
-    }
-    const int off = (p0 % BS) + (lane & 15);
-    // plain MFMA order: K-step s takes dims 32*s + 8*(lane/16) .. +7
-    const uint4* src = reinterpret_cast<const uint4*>(cache + ((int64_t)phys * BS + off) * 256 +
-                                                      16 * (lane >> 4));
-#pragma unroll
-    for (int s = 0; s < 4; ++s) raw.c[g][s] = src[4 * s];
-  }
-}
 
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   union {
@@ -109,171 +75,64 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return x.b;
 }
 
-template <int BS>
-__global__ __launch_bounds__(256, 2) void score_decode_bf16_kernel(
-    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
-    int64_t num_blocks, const int32_t* __restrict__ block_table, int max_blocks, int num_seqs,
-    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_len, int max_row_len,
-    float* __restrict__ scores, int64_t ld, int spans_per_wave, int write_pad) {
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = blockIdx.y;
-  const int seq = row_seq[r];
-  const int n = min(max(row_len[r], 0), max_row_len);
-  float* out = scores + (int64_t)r * ld;
-  constexpr int KS = kSpan;
-  const int chunk0 = blockIdx.x * (4 * spans_per_wave * KS);
-  const bool seq_bad = seq < 0 || seq >= num_seqs;
-
-  if (chunk0 >= n || seq_bad) {  // nothing to read: padding, or NaN for a bad sequence
-    const int end = min(chunk0 + 4 * spans_per_wave * KS, max_row_len);
-    for (int p = chunk0 + (int)threadIdx.x; p < end; p += 256) {
-      if (p < n) out[p] = __builtin_nanf("");
-      else if (write_pad) out[p] = -INFINITY;
-    }
-    return;
-  }
-
-  // The query row and head weights pass through LDS once per workgroup (every wave
-  // needs all of them as operands; four copies from L2 cost more than the MFMA
-  // work).  Chunk c (16 bytes) of head h sits at c ^ (h % 16) within the head's 256
-  // bytes, so the eight lanes of a 16-byte read phase hit distinct banks.
-  __shared__ uint4 qst[kQRowBytes / 16 + 16];
-  {
-    const uint4* qrow = reinterpret_cast<const uint4*>(q + (int64_t)r * 64 * kHeadDim);
-    uint4 x[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = qrow[j * 256 + threadIdx.x];
-    float wr = 0.0f;
-    if (threadIdx.x < 64) wr = w[(int64_t)r * 64 + threadIdx.x];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = j * 256 + threadIdx.x, h = i >> 4;
-      qst[h * 16 + ((i & 15) ^ (h & 15))] = x[j];
-    }
-    if (threadIdx.x < 64) reinterpret_cast<float*>(qst + kQRowBytes / 16)[threadIdx.x] = wr;
-    lds_barrier();
-  }
-  // A operands in the plain MFMA order: K-step s of M tile mt holds head
-  // 16*mt + lane%16, dims 32*s + 8*(lane/16) .. +7 (chunk 4*s + lane/16).  wv: weights
-  // of the accumulator rows, head 16*mt + 4*(lane/16) + v.
-  bf16x8_t qa[4][4];
-  float wv[4][4];
-  {
-    const int hl = lane & 15, g4 = lane >> 4;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        qa[mt][s] = as_bf16x8(qst[(16 * mt + hl) * 16 + ((4 * s + g4) ^ hl)]);
-      }
-      const float4 wq = reinterpret_cast<const float4*>(qst + kQRowBytes / 16)[4 * mt + g4];
-      wv[mt][0] = wq.x;
-      wv[mt][1] = wq.y;
-      wv[mt][2] = wq.z;
-      wv[mt][3] = wq.w;
-    }
-  }
-
-  const int32_t* bt_row = block_table + (int64_t)seq * max_blocks;
-
-  SpanRaw cur, nxt;
-  uint32_t cur_bad = 0, nxt_bad = 0;
-  int p_span = chunk0 + wave * KS;
-  if (p_span < n) load_span<BS>(cur, cur_bad, cache, num_blocks, bt_row, p_span, n, lane);
-
-  for (int i = 0; i < spans_per_wave; ++i, p_span += 4 * KS) {
-    const int p_next = p_span + 4 * KS;
-    if (i + 1 < spans_per_wave && p_next < n)
-      load_span<BS>(nxt, nxt_bad, cache, num_blocks, bt_row, p_next, n, lane);
-
-    if (p_span < n) {
-#pragma unroll
-      for (int sub = 0; sub < KS / 64; ++sub) {  // 64 keys: four 16-key groups
-        float val = 0.0f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int gg = 4 * sub + g;
-          f32x4_t acc[4];
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8_t b = as_bf16x8(cur.c[gg][s]);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], b, acc[mt], 0, 0, 0);
-          }
-          float part = 0.0f;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) part = fmaf(wv[mt][v], relu(acc[mt][v]), part);
-          part = rows4_sum(part);
-          if ((lane >> 4) == g) val = part + 0.0f;  // +0.0f: a zero score is +0
-        }
-        const int p = p_span + 64 * sub + lane;
-        if (p >= n) val = -INFINITY;
-        if ((cur_bad >> (4 * sub + (lane >> 4))) & 1u) val = __builtin_nanf("");
-        if (p < max_row_len) out[p] = val;
-      }
-    } else if (write_pad) {
-#pragma unroll
-      for (int sub = 0; sub < KS / 64; ++sub) {
-        const int p = p_span + 64 * sub + lane;
-        if (p < max_row_len) out[p] = -INFINITY;
-      }
-    }
-    cur = nxt;
-    cur_bad = nxt_bad;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// fp8 and MXFP4 keys: the same tiling, with the key stream moved to LDS DMA.  Each
-// wave owns a ring of kRing 16-key group slots in LDS and keeps kRing-1 groups in
-// flight with global_load_lds (no VGPRs held by loads in flight), so far more bytes
-// are outstanding per wave than a register double buffer allows at 2 waves per SIMD.
-// Every group issues a fixed number of loads (fp8: 2 x 1 KB of codes and 64 B of
-// scales; MXFP4: 1 KB of codes and 64 B of e8m0 scales), so a fixed vmcnt wait
-// guarantees the group about to be read has landed; the score stores interleaved
-// with the loads only make that wait stricter.  Within a slot, 16-byte code chunks
-// are XOR-swizzled by key so a read phase (several keys, same chunk) hits distinct
-// banks: fp8 chunk c of key r sits at position r*8 + (c ^ ((r >> 1) & 7)), MXFP4
-// chunk c at r*4 + (c ^ ((r >> 2) & 3)).
-constexpr int kGroupCodes = 16 * 128;
-constexpr int kGroupSlot = kGroupCodes + 16 * 4;  // 2112 bytes
-constexpr int kGroupCodes4 = 16 * 64;
-constexpr int kGroupSlot4 = kGroupCodes4 + 16 * 4;  // 1088 bytes
+// The key stream goes through LDS DMA.  Each wave owns a ring of kRing 16-key group
+// slots in LDS and keeps kRing-1 groups in flight with global_load_lds (no VGPRs
+// held by loads in flight), so far more bytes are outstanding per wave than a
+// register double buffer allows (bf16 spans held in registers took 232 VGPRs, 2
+// waves per SIMD).  Every group issues a fixed number of loads (fp8: 2 x 1 KB of
+// codes and 64 B of scales; MXFP4: 1 KB of codes and 64 B of e8m0 scales; bf16:
+// 4 x 1 KB), so a fixed vmcnt wait guarantees the group about to be read has
+// landed; the score stores interleaved with the loads only make that wait
+// stricter.  Within a slot, 16-byte chunks are XOR-swizzled by key so a read phase
+// (several keys, same chunk) hits distinct banks: fp8 chunk c of key r sits at
+// position r*8 + (c ^ ((r >> 1) & 7)), MXFP4 chunk c at r*4 + (c ^ ((r >> 2) & 3)),
+// bf16 chunk c at r*16 + (c ^ r).
 #ifndef DSA_DECODE_RING
 #define DSA_DECODE_RING 3
 #endif
 #ifndef DSA_DECODE_RING4
 #define DSA_DECODE_RING4 6
 #endif
-constexpr int kDecodeRing = DSA_DECODE_RING;    // LDS slots per wave, fp8 keys
-constexpr int kDecodeRing4 = DSA_DECODE_RING4;  // MXFP4 keys (smaller slots, deeper ring)
+#ifndef DSA_DECODE_RING16
+#define DSA_DECODE_RING16 3
+#endif
+constexpr int kDecodeRing = DSA_DECODE_RING;      // LDS slots per wave, fp8 keys
+constexpr int kDecodeRing4 = DSA_DECODE_RING4;    // MXFP4 keys (smaller slots, deeper ring)
+constexpr int kDecodeRing16 = DSA_DECODE_RING16;  // bf16 keys (4 KB slots)
 
-template <bool kFp4>
+template <int kKind>
 struct RingKeys {
-  static constexpr int kCodes = kFp4 ? kGroupCodes4 : kGroupCodes;  // code bytes of a group
-  static constexpr int kSlot = kFp4 ? kGroupSlot4 : kGroupSlot;
-  static constexpr int kKeyBytes = kFp4 ? 68 : 132;  // cache bytes per token
-  static constexpr int kLoads = kFp4 ? 2 : 3;        // load instructions per group
+  static constexpr bool kFp4 = kKind == kFp4Keys, kBf16 = kKind == kBf16Keys;
+  static constexpr int kRow = kBf16 ? 256 : (kFp4 ? 64 : 128);  // key bytes before the scales
+  static constexpr int kCodes = 16 * kRow;                         // code bytes of a group
+  static constexpr int kSlot = kCodes + (kBf16 ? 0 : 16 * 4);      // + the 16 keys' scale words
+                                                                   // (fp8 2112, MXFP4 1088, bf16 4096 bytes)
+  static constexpr int kKeyBytes = kBf16 ? 256 : (kFp4 ? 68 : 132);  // cache bytes per token
+  static constexpr int kLoads = kBf16 ? 4 : (kFp4 ? 2 : 3);          // load instructions per group
 };
 
-// Every key group is read once.  fp8 groups are loaded with the non-temporal cache
-// policy (NT), which leaves L2 to the query rows and block tables: measured 8%
-// faster on decode batch 32 and 4% on 16 x 128k keys.  MXFP4 groups, at half the
-// bytes, measured no gain and keep the default policy.
-template <int BS, bool kFp4>
+// Every key group is read once.  fp8 and bf16 groups are loaded with the
+// non-temporal cache policy (NT), which leaves L2 to the query rows and block
+// tables: measured 8% faster on decode batch 32 with fp8 keys, 4% on 16 x 128k fp8
+// keys and 12% on 16 x 128k bf16 keys.  MXFP4 groups, at half the bytes, measured
+// no gain and keep the default policy.
+template <int BS, int kKind>
 __device__ __forceinline__ void issue_group(uint8_t* slot, const uint8_t* cache, int phys, int p0, int lane) {
   typedef __attribute__((address_space(3))) void lds_void;
-  constexpr int kCodeRow = kFp4 ? 64 : 128;  // code bytes per key
-  constexpr int kCpol = kFp4 ? 0 : 2;        // cache policy bits of the loads: 2 = NT
-  const uint8_t* blk = cache + (int64_t)phys * (BS * RingKeys<kFp4>::kKeyBytes);
+  using K = RingKeys<kKind>;
+  constexpr int kCpol = K::kFp4 ? 0 : 2;  // cache policy bits of the loads: 2 = NT
+  const uint8_t* blk = cache + (int64_t)phys * (BS * K::kKeyBytes);
   const int off = p0 % BS;
-  if constexpr (kFp4) {
+  if constexpr (K::kBf16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sidx = j * 64 + lane, r = sidx >> 4, c = (sidx & 15) ^ r;
+      __builtin_amdgcn_global_load_lds(blk + (off + r) * 256 + c * 16,
+                                       (lds_void*)(slot + j * 1024), 16, 0, kCpol);
+    }
+    return;  // (no scales)
+  } else if constexpr (K::kFp4) {
     const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
     __builtin_amdgcn_global_load_lds(blk + (off + r) * 64 + c * 16, (lds_void*)slot, 16, 0, kCpol);
   } else {
@@ -285,11 +144,11 @@ __device__ __forceinline__ void issue_group(uint8_t* slot, const uint8_t* cache,
     }
   }
   if (lane < 16)  // the 16 keys' scale words (fp32, or four e8m0 bytes)
-    __builtin_amdgcn_global_load_lds(blk + BS * kCodeRow + (off + lane) * 4,
-                                     (lds_void*)(slot + RingKeys<kFp4>::kCodes), 4, 0, kCpol);
+    __builtin_amdgcn_global_load_lds(blk + BS * K::kRow + (off + lane) * 4,
+                                     (lds_void*)(slot + K::kCodes), 4, 0, kCpol);
 }
 
-template <int BS, int kRing, bool kFp4>
+template <int BS, int kRing, int kKind>
 __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ cache,
     int64_t num_blocks, const int32_t* __restrict__ block_table, int max_blocks, int num_seqs,
@@ -298,7 +157,8 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
   // ring[slot][wave]: slot s of the four waves is contiguous, so slots 1 .. kRing-1
   // together hold the 16 KB query row while it is staged (they are free until the
   // wave issues its second group)
-  constexpr int kSlot = RingKeys<kFp4>::kSlot;
+  constexpr bool kFp4 = RingKeys<kKind>::kFp4, kBf16 = RingKeys<kKind>::kBf16;
+  constexpr int kSlot = RingKeys<kKind>::kSlot;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][4][kSlot];
   static_assert((kRing - 1) * 4 * kSlot >= kQRowBytes + 256, "query row and weights fit the staging slots");
   const int lane = lane_id();
@@ -361,9 +221,9 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
     if (wave == 0)
       __builtin_amdgcn_global_load_lds(w + (int64_t)r * 64 + lane, (lds_void*)(qs + kQRowBytes), 4, 0, 0);
   }
-  issue_group<BS, kFp4>(my(0), cache, __builtin_amdgcn_readlane(my_phys, 0), group_pos(0), lane);
+  issue_group<BS, kKind>(my(0), cache, __builtin_amdgcn_readlane(my_phys, 0), group_pos(0), lane);
   // every wave's share landed (group 0's loads may stay in flight)
-  __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(RingKeys<kFp4>::kLoads) : "memory");
+  __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(RingKeys<kKind>::kLoads) : "memory");
 
   // A operands: K-step s4 of M tile mt holds head 16*mt + lane%16 and, for fp8 keys,
   // dims 32*s4 + 8*(lane/16) .. +7 (chunk 4*s4 + lane/16, the plain MFMA order); for
@@ -406,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
   __asm__ volatile("s_barrier" ::: "memory");  // every wave has its operands: the slots are free
 #pragma unroll
   for (int t = 1; t < kRing - 1; ++t)
-    issue_group<BS, kFp4>(my(t), cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
+    issue_group<BS, kKind>(my(t), cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
 
 
   // read positions of this lane in a slot: key lane%16; fp8: dims 32*s4 + 8*(lane/16)
@@ -415,7 +275,10 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
   const int kr = lane & 15;
   const int g4 = lane >> 4;
   int rd[4];
-  if constexpr (kFp4) {
+  if constexpr (kBf16) {  // chunk 4*s4 + lane/16 of key kr (dims 32*s4 + 8*(lane/16) .. +7)
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) rd[s4] = kr * 256 + (((4 * s4 + g4) ^ kr) << 4);
+  } else if constexpr (kFp4) {
     rd[0] = kr * 64 + ((g4 ^ ((kr >> 2) & 3)) << 4);
     rd[1] = rd[2] = rd[3] = rd[0];
   } else {
@@ -429,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
   int wslot = kRing - 1, rslot = 0;
   for (int t = 0; t < ngroups; ++t) {
     const int tn = t + kRing - 1;  // (readlane of a lane >= ngroups gives block 0)
-    issue_group<BS, kFp4>(my(wslot), cache, __builtin_amdgcn_readlane(my_phys, tn & 63), group_pos(tn), lane);
+    issue_group<BS, kKind>(my(wslot), cache, __builtin_amdgcn_readlane(my_phys, tn & 63), group_pos(tn), lane);
     wslot = wslot == kRing - 1 ? 0 : wslot + 1;
     // wait for group t (3 loads x (kRing - 1) newer groups may stay in flight), then
     // read this lane's two code chunks and its key's scale; the waits sit in the asm
@@ -439,9 +302,23 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
     // the slot's codes: fp8, four 8-byte halves (one per K-step); MXFP4, one 16-byte
     // chunk (one dword per K-step) and the key's four e8m0 bytes
     uint2 c[4];
-    float ks;  // the key's scale (fp8), or 1 (MXFP4: the block scale is in the B operand)
+    uint4 cb[4];  // bf16 keys: the four K-steps' 16-byte operands
+    float ks;     // the key's scale (fp8), or 1 (MXFP4: the block scale is in the B operand)
     float bscale = 1.0f;
-    if constexpr (kFp4) {
+    if constexpr (kBf16) {
+      __asm__ volatile(
+          "s_waitcnt vmcnt(%8)\n\t"
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(cb[0]), "=&v"(cb[1]), "=&v"(cb[2]), "=&v"(cb[3])
+          : "v"(sbase + rd[0]), "v"(sbase + rd[1]), "v"(sbase + rd[2]), "v"(sbase + rd[3]),
+            "n"(4 * (kRing - 1))
+          : "memory");
+      ks = 1.0f;
+    } else if constexpr (kFp4) {
       uint4 c4;
       uint32_t sw4;
       __asm__ volatile(
@@ -450,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
           "ds_read_b32 %1, %3\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(c4), "=&v"(sw4)
-          : "v"(sbase + rd[0]), "v"(sbase + kGroupCodes4 + 4 * kr), "n"(2 * (kRing - 1))
+          : "v"(sbase + rd[0]), "v"(sbase + RingKeys<kKind>::kCodes + 4 * kr), "n"(2 * (kRing - 1))
           : "memory");
       const uint32_t e8 = (sw4 >> (8 * g4)) & 0xFFu;
       bscale = __uint_as_float(e8 ? e8 << 23 : 0x00400000u);  // 2^(e8-127)
@@ -470,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(ks)
           : "v"(sbase + rd[0]), "v"(sbase + rd[1]), "v"(sbase + rd[2]), "v"(sbase + rd[3]),
-            "v"(sbase + kGroupCodes + 4 * kr), "n"(3 * (kRing - 1))
+            "v"(sbase + RingKeys<kKind>::kCodes + 4 * kr), "n"(3 * (kRing - 1))
           : "memory");
     }
     const int p0 = group_pos(t);
@@ -480,7 +357,8 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const bf16x8_t b = kFp4 ? fp4x8_to_bf16x8(c[s4].x, bscale) : fp8x8_to_bf16x8(c[s4].x, c[s4].y);
+      const bf16x8_t b = kBf16 ? as_bf16x8(cb[s4])
+                               : (kFp4 ? fp4x8_to_bf16x8(c[s4].x, bscale) : fp8x8_to_bf16x8(c[s4].x, c[s4].y));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s4], b, acc[mt], 0, 0, 0);
@@ -528,20 +406,14 @@ hipError_t launch_bs(const uint16_t* q, const float* w, const KCache& c, const R
                      c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq, r.row_len, \
                      r.max_row_len, scores, ld, spw, (int)write_pad)
   if constexpr (kKeys == kFp8Keys) {  // fp8 keys: the LDS-ring kernel
-    if (c.block_size == 64) DSA_RING_LAUNCH(64, kDecodeRing, false);
-    else DSA_RING_LAUNCH(32, kDecodeRing, false);
-  } else if constexpr (kKeys == kFp4Keys) {  // MXFP4 keys: the LDS-ring kernel
-    if (c.block_size == 64) DSA_RING_LAUNCH(64, kDecodeRing4, true);
-    else DSA_RING_LAUNCH(32, kDecodeRing4, true);
-  } else {  // bf16 keys: the register-streaming kernel
-    if (c.block_size == 64)
-      hipLaunchKernelGGL((score_decode_bf16_kernel<64>), grid, block, 0, s, q, w, c.base,
-                         c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
-                         r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
-    else
-      hipLaunchKernelGGL((score_decode_bf16_kernel<32>), grid, block, 0, s, q, w, c.base,
-                         c.num_blocks, r.block_table, r.max_blocks, r.num_seqs, r.row_seq,
-                         r.row_len, r.max_row_len, scores, ld, spw, (int)write_pad);
+    if (c.block_size == 64) DSA_RING_LAUNCH(64, kDecodeRing, kFp8Keys);
+    else DSA_RING_LAUNCH(32, kDecodeRing, kFp8Keys);
+  } else if constexpr (kKeys == kFp4Keys) {  // MXFP4 keys
+    if (c.block_size == 64) DSA_RING_LAUNCH(64, kDecodeRing4, kFp4Keys);
+    else DSA_RING_LAUNCH(32, kDecodeRing4, kFp4Keys);
+  } else {  // bf16 keys
+    if (c.block_size == 64) DSA_RING_LAUNCH(64, kDecodeRing16, kBf16Keys);
+    else DSA_RING_LAUNCH(32, kDecodeRing16, kBf16Keys);
   }
 #undef DSA_RING_LAUNCH
   return hipGetLastError();
