@@ -225,8 +225,9 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
   // every wave's share landed (group 0's loads may stay in flight)
   __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(RingKeys<kKind>::kLoads) : "memory");
 
-  // A operands: K-step s4 of M tile mt holds head 16*mt + lane%16 and, for fp8 keys,
-  // dims 32*s4 + 8*(lane/16) .. +7 (chunk 4*s4 + lane/16, the plain MFMA order); for
+  // A operands: K-step s4 of M tile mt holds head 16*mt + lane%16 and, for fp8 and
+  // bf16 keys, dims 32*s4 + 8*(lane/16) .. +7 (chunk 4*s4 + lane/16, the plain MFMA
+  // order); for
   // MXFP4 keys, whose lane keeps one whole 32-dim scale block, dims 32*(lane/16) +
   // 8*s4 .. +7 (chunk 4*(lane/16) + s4)
   // wv: weights of the accumulator rows this lane holds, head 16*mt + 4*(lane/16) + v
@@ -268,10 +269,10 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
   for (int t = 1; t < kRing - 1; ++t)
     issue_group<BS, kKind>(my(t), cache, __builtin_amdgcn_readlane(my_phys, t), group_pos(t), lane);
 
-
   // read positions of this lane in a slot: key lane%16; fp8: dims 32*s4 + 8*(lane/16)
   // .. +7, i.e. half (lane/16)&1 of code chunk 2*s4 + lane/32; MXFP4: code chunk
-  // lane/16 (dims 32*(lane/16) .. +31) and scale byte lane/16 of the key's word
+  // lane/16 (dims 32*(lane/16) .. +31) and scale byte lane/16 of the key's word;
+  // bf16: one 16-byte chunk per K-step
   const int kr = lane & 15;
   const int g4 = lane >> 4;
   int rd[4];
@@ -294,9 +295,10 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
     const int tn = t + kRing - 1;  // (readlane of a lane >= ngroups gives block 0)
     issue_group<BS, kKind>(my(wslot), cache, __builtin_amdgcn_readlane(my_phys, tn & 63), group_pos(tn), lane);
     wslot = wslot == kRing - 1 ? 0 : wslot + 1;
-    // wait for group t (3 loads x (kRing - 1) newer groups may stay in flight), then
-    // read this lane's two code chunks and its key's scale; the waits sit in the asm
-    // because the compiler would otherwise drain every load before any LDS read
+    // wait for group t (the kLoads loads of each of the kRing - 1 newer groups may
+    // stay in flight), then read this lane's operands and its key's scale; the waits
+    // sit in the asm because the compiler would otherwise drain every load before any
+    // LDS read
     const uint32_t sbase = (uint32_t)(uintptr_t)my(rslot);
     rslot = rslot == kRing - 1 ? 0 : rslot + 1;
     // the slot's codes: fp8, four 8-byte halves (one per K-step); MXFP4, one 16-byte
