@@ -50,13 +50,14 @@ def test_score_matches_oracle(cfg, scale, kd, bs):
     print(stats)
 
 
-def test_page_table_permutation_is_bit_invariant():
+@pytest.mark.parametrize("kd", ["fp8", "bf16", "fp4"])
+def test_page_table_permutation_is_bit_invariant(kd):
     # identical logical keys behind the identity table and behind a shuffled one
     wl_id = gen.config(2, scale=0.05, shuffle=False)
     wl_sh = gen.config(2, scale=0.05, shuffle=True)
     assert not np.array_equal(wl_id.block_table, wl_sh.block_table)
-    a = gpu_scores(GpuWorkload(wl_id))
-    b = gpu_scores(GpuWorkload(wl_sh))
+    a = gpu_scores(GpuWorkload(wl_id, key_dtype=kd))
+    b = gpu_scores(GpuWorkload(wl_sh, key_dtype=kd))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
@@ -68,15 +69,17 @@ def test_deterministic_and_ld_independent():
     assert np.array_equal(a[:, :wl.max_row_len].view(np.uint32), b[:, :wl.max_row_len].view(np.uint32))
 
 
-def test_ragged_rows_and_edge_lengths():
-    # rows of length 0, 1, 15, 16, 17, 63, 64, 65 and one spanning many blocks
+@pytest.mark.parametrize("kd,bs", [("fp8", 64), ("bf16", 64), ("fp4", 64), ("fp8", 32), ("bf16", 32), ("fp4", 32)])
+def test_ragged_rows_and_edge_lengths(kd, bs):
+    # rows of length 0, 1, 15, 16, 17, 63, 64, 65 and one spanning many blocks: a
+    # workgroup's waves then hold from zero to many key groups
     lens = np.array([0, 1, 15, 16, 17, 63, 64, 65, 777], np.int64)
-    wl = gen.make(np.maximum(lens, 1), key_dtype="fp8", k=4, needle_depth=None, seed=5)
+    wl = gen.make(np.maximum(lens, 1), key_dtype=kd, k=4, needle_depth=None, block_size=bs, seed=5)
     wl.row_len = lens.astype(np.int32)
-    g = GpuWorkload(wl)
+    g = GpuWorkload(wl, key_dtype=kd)
     got = gpu_scores(g)
-    o = oracle_scores(wl, OracleKeys(wl))
-    check_scores(got, o, wl.row_len, RTOL["fp8"])
+    o = oracle_scores(wl, OracleKeys(wl, kd))
+    check_scores(got, o, wl.row_len, RTOL[kd])
 
 
 def test_rows_sharing_a_sequence():
