@@ -114,11 +114,12 @@ typedef struct {
 
 /*
  * index_k_store - write n index keys into the paged cache.
- * Steps ([PIVOT-EDIT] "The Reasoning Behind the Edit": normalise, RoPE, rotate, then
- * store; [ATOM-1507] "Root cause found"/"Where": interleaved RoPE on the trailing
- * rope_dim, then the Walsh-Hadamard rotation that must match the query's; the
- * store is the analog of the pages' indexer_k_quant_and_cache / fused compressor
- * store), each enabled by a flag:
+ * Steps ([PIVOT-EDIT] "The Reasoning Behind the Edit": the unfused key path
+ * normalises, applies RoPE and rotates before it writes the cache; [ATOM-1507]
+ * "Root cause found"/"Where": interleaved RoPE on the trailing rope_dim, then the
+ * Walsh-Hadamard rotation that must match the query's; the store is the analog of
+ * the pages' indexer_k_quant_and_cache / fused compressor store), each enabled by a
+ * flag:
  *   RMSNorm   y = x / sqrt(mean(x^2) + rms_eps), unit gain
  *   RoPE      pair i = (y[o+2i], y[o+2i+1]), o = 128 - rope_dim, rotated by
  *             pos * rope_base^(-2i/rope_dim) (angle formed in double precision)
@@ -167,8 +168,8 @@ int32_t index_k_store(const void* x_bf16, int64_t n, const int32_t* positions,
  *   codes, scales both NULL, or device uint8 [n_vec][128] and fp32 [n_vec].
  *   prequant_dbg  NULL or device fp32 [n_vec][128]: y before rounding/quantisation.
  * At least one output must be requested.  Errors: IDX_EINVAL for a bad size, flag,
- * rope parameter, missing pointer or misaligned pointer (q_bf16, out_bf16, scales
- * 4-byte; codes 2-byte; prequant_dbg 8-byte).
+ * rope parameter, missing pointer or misaligned pointer (q_bf16, out_bf16 and
+ * prequant_dbg 16-byte; codes 8-byte; scales and positions 4-byte).
  */
 int32_t indexer_q_prep(const void* q_bf16, int64_t n_vec, int32_t heads, const int32_t* positions,
                        uint32_t flags, float rms_eps, float rope_base, int32_t rope_dim, void* out_bf16,
@@ -201,7 +202,9 @@ int32_t indexer_quant_fp8(const void* x_bf16, int64_t n_vec, uint8_t* codes, flo
  *   heads    64 (v1).
  *   scores   device fp32 [rows][ld], ld >= max_row_len; columns >= max_row_len are
  *            not written.
- * Supported (q, key) dtypes: (bf16, bf16), (bf16, fp8), (fp8, fp8).
+ * Supported (q, key) dtypes: (bf16, bf16), (bf16, fp8), (bf16, MXFP4), (fp8, fp8),
+ * (fp8, MXFP4).  (fp8, bf16) returns IDX_EUNSUPPORTED.  A key whose block id lies
+ * outside [0, num_blocks) scores NaN; only that block's keys are affected.
  */
 int32_t indexer_score(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
                       int32_t heads, idx_kcache cache, idx_rows rows, float* scores, int64_t ld,

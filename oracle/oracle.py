@@ -24,6 +24,8 @@ the rest of the pages support.
 
 Pin status of every public function (what fixes it other than itself is in
 tests/test_oracle_*.py):
+  bf16_bits_to_f64, bf16_round ............ pinned (torch bfloat16 on every bit
+                                             pattern and on a sample of float32)
   e4m3_decode, e4m3_encode, quant_fp8 ..... pinned (format definition values,
                                              torch float8_e4m3fn, exact rationals)
   hadamard_matrix, rmsnorm, rope,
@@ -39,8 +41,10 @@ tests/test_oracle_*.py):
                                              bound, a hand-worked block)
   score, score_rows ....................... pinned (exact-rational brute force,
                                              closed forms, invariants)
-  topk ..................................... pinned (subset brute force, numpy and
-                                             torch library routines)
+  topk, kth_score ........................... pinned (subset brute force, numpy and
+                                             torch library routines; a hand-worked
+                                             row with ties; the order-statistic
+                                             counting definition)
   translate ................................ pinned (hand-worked example, the
                                              identity table's closed form, the
                                              store's slot of every stored position,
@@ -69,6 +73,31 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32)
+
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bf16 value of each finite float32 (ties to the even last mantissa
+    bit), as uint16 bit patterns.  The bf16 store keeps a key this way
+    ([PIVOT-EDIT] "Assumptions and Input Knowledge": 256 bytes per bf16 token).
+
+    The two candidates are the bf16 values just below and just above |x| in
+    magnitude (the float32 with its low 16 bits cleared, and the next bf16 up);
+    |x| is compared with their midpoint exactly in float64."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x32)):
+        raise ValueError("bf16_round: finite inputs only")
+    u = x32.view(np.uint32)
+    sign = u & np.uint32(0x80000000)
+    lo = u & np.uint32(0x7FFF0000)                       # magnitude truncated to bf16
+    hi = lo + np.uint32(0x10000)                          # next bf16 magnitude up
+    a = np.abs(x32.astype(np.float64))
+    v_lo = lo.view(np.float32).astype(np.float64)
+    v_hi = hi.view(np.float32).astype(np.float64)         # (may be +inf: then a < mid)
+    mid = (v_lo + v_hi) / 2.0
+    odd = ((lo >> np.uint32(16)) & np.uint32(1)) == 1
+    pick_hi = (a > mid) | ((a == mid) & odd)
+    mag = np.where(pick_hi, hi, lo)
+    return ((mag | sign) >> np.uint32(16)).astype(np.uint16)
 
 
 # ----------------------------------------------------------------------------------
@@ -229,9 +258,10 @@ def dequant_mxfp4(codes, e8m0, block: int = 32) -> np.ndarray:
 
 # ----------------------------------------------------------------------------------
 # Index-K store chain: RMSNorm -> RoPE -> Hadamard -> (quantise) -> paged write.
-# Order from [PIVOT-EDIT] "The Reasoning Behind the Edit" (normalisation, RoPE and
-# rotation as separate steps before storing) and [ATOM-1507] "Where" (interleaved
-# RoPE on the trailing rope_dim, then the Walsh-Hadamard rotation).
+# Order: [PIVOT-EDIT] "The Reasoning Behind the Edit" describes an unfused key path
+# that normalises the key, applies its rotary embedding and rotates it, and only
+# then writes it to the cache; [ATOM-1507] "Where" puts the interleaved RoPE on the
+# trailing rope_dim ahead of the Walsh-Hadamard rotation.
 # ----------------------------------------------------------------------------------
 
 STORE_RMSNORM = 1

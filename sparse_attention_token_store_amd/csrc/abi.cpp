@@ -169,13 +169,15 @@ IDX_API int32_t indexer_q_prep(const void* q_bf16, int64_t n_vec, int32_t heads,
   if ((n_vec / heads) * (((int64_t)heads + 3) / 4) > (int64_t)INT32_MAX * 4)
     return fail(IDX_EINVAL, "too many vectors for one launch (rows * ceil(heads / 4) > 4 * INT32_MAX)");
   if (!q_bf16) return fail(IDX_EINVAL, "q_bf16 must be non-NULL");
-  if (!aligned(q_bf16, 4)) return fail(IDX_EINVAL, "q_bf16 must be 4-byte aligned");
+  // the kernel moves 16-byte chunks of q, out_bf16 and prequant_dbg and 8-byte
+  // chunks of codes
+  if (!aligned(q_bf16, 16)) return fail(IDX_EINVAL, "q_bf16 must be 16-byte aligned");
   if ((flags & IDX_STORE_ROPE) && !positions) return fail(IDX_EINVAL, "positions is required with IDX_STORE_ROPE");
   if (positions && !aligned(positions, 4)) return fail(IDX_EINVAL, "positions must be 4-byte aligned");
-  if (out_bf16 && !aligned(out_bf16, 4)) return fail(IDX_EINVAL, "out_bf16 must be 4-byte aligned");
-  if (codes && !aligned(codes, 2)) return fail(IDX_EINVAL, "codes must be 2-byte aligned");
+  if (out_bf16 && !aligned(out_bf16, 16)) return fail(IDX_EINVAL, "out_bf16 must be 16-byte aligned");
+  if (codes && !aligned(codes, 8)) return fail(IDX_EINVAL, "codes must be 8-byte aligned");
   if (scales && !aligned(scales, 4)) return fail(IDX_EINVAL, "scales must be 4-byte aligned");
-  if (prequant_dbg && !aligned(prequant_dbg, 8)) return fail(IDX_EINVAL, "prequant_dbg must be 8-byte aligned");
+  if (prequant_dbg && !aligned(prequant_dbg, 16)) return fail(IDX_EINVAL, "prequant_dbg must be 16-byte aligned");
   return launched(dsa::launch_q_prep(static_cast<const uint16_t*>(q_bf16), n_vec, heads, positions, flags,
                                      rms_eps, rope_base, rope_dim, static_cast<uint16_t*>(out_bf16), codes,
                                      scales, prequant_dbg, static_cast<hipStream_t>(hip_stream)),

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
   }
 
   float val = 0.0f;
-  bool bad = false;
+  uint32_t bad = 0;  // bit g: group g of the current span lies in a bad block
   int wslot = kRing - 1, rslot = 0;
   for (int t = 0; t < ngroups; ++t) {
     const int tn = t + kRing - 1;  // (readlane of a lane >= ngroups gives block 0)
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
           : "memory");
     }
     const int p0 = group_pos(t);
-    bad = bad || ((bad_groups >> t) & 1);
+    bad |= (uint32_t)((bad_groups >> t) & 1) << (t & 3);
     f32x4_t acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -375,11 +375,11 @@ __global__ __launch_bounds__(256, 2) void score_decode_ring_kernel(
     if ((t & 3) == 3 || t + 1 == ngroups) {  // end of a span: one coalesced store
       const int p = (p0 & ~(kSpan - 1)) + lane;
       float v = val;
-      if (bad) v = __builtin_nanf("");
+      if ((bad >> (lane >> 4)) & 1u) v = __builtin_nanf("");  // only the bad block's keys
       if (p >= n) v = -INFINITY;
       if (p < max_row_len) out[p] = v;
       val = 0.0f;
-      bad = false;
+      bad = 0;
     }
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the ring before the wave ends

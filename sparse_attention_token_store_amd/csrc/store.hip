@@ -1,10 +1,11 @@
 // Index-K store and the contiguous fp8 quantiser.
 //
 // Store chain per token ("The Pivot: A Single Edit That Finally Fixed DeepSeek V4's
-// Long-Context Recall Failure", "The Reasoning Behind the Edit": normalise, RoPE and
-// rotate before the store; ROCm/ATOM issue 1507, "Root cause found" and "Where":
-// interleaved RoPE on the trailing rope_dim, then the Walsh-Hadamard rotation the
-// key must share with the query), fused into one pass over registers:
+// Long-Context Recall Failure", "The Reasoning Behind the Edit": the unfused key
+// path normalises, applies RoPE and rotates, and writes the cache last; ROCm/ATOM
+// issue 1507, "Root cause found" and "Where": interleaved RoPE on the trailing
+// rope_dim, then the Walsh-Hadamard rotation the key must share with the query),
+// fused into one pass over registers:
 //   RMSNorm -> RoPE -> 128-point Hadamard -> fp8 absmax quantise (or bf16 round)
 //   -> scatter into the paged cache.
 // The query preparation runs the same chain on every query vector (the query must

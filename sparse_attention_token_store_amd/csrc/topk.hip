@@ -58,8 +58,14 @@ struct Lists {  // candidate lists of one level: keys and positions, [rows][cap]
   int64_t cap;
 };
 
+// Levels a row can need: the first level halves a row at worst (k = 8192 keeps 8192
+// of every 16,384), every later one keeps at most 1 in 4 (k of >= 4k), so a row of
+// INT32_MAX elements reaches one 36,864-element chunk after 9 reducing levels (10
+// with the last); 12 leaves room.
+constexpr int kMaxLevels = 12;
+
 struct LevelChunks {  // chunk size of every level, passed by value
-  int64_t c[8];
+  int64_t c[kMaxLevels];
 };
 
 // Inclusive scan over the 64 lanes of a wavefront with the gfx9 DPP row shifts:
@@ -545,8 +551,8 @@ hipError_t launch_level(int R, dim3 grid, hipStream_t s, const float* scores, in
 // size of level l; the last level has a single chunk.
 struct Plan {
   int levels = 0;
-  int64_t chunk[8];
-  int64_t len[9];  // worst-case list length entering level l
+  int64_t chunk[kMaxLevels];
+  int64_t len[kMaxLevels + 1];  // worst-case list length entering level l
 };
 
 int pick_r(int64_t n) {
@@ -559,7 +565,7 @@ Plan make_plan(int max_row_len, int k) {
   Plan p;
   int64_t n = max_row_len;
   p.len[0] = n;
-  while (n > kMaxSingle) {
+  while (n > kMaxSingle && p.levels < kMaxLevels - 1) {  // (the bound never binds: see kMaxLevels)
     // first level: 16,384-element chunks (at least 2k); later levels: chunks of 8k
     // (a power of two, at most 32,768), so a level keeps 1 in 8 and still spreads a
     // few long rows over many workgroups

@@ -6,10 +6,10 @@ draws random numbers and lays them out; it computes none of the indexer's arithm
 
 Key distribution: a Gaussian mixture (256 centres ~ N(0,1)^128, per-key noise with
 sd 0.3), q ~ N(0,1), head weights w ~ U(0,1)/8, with one "needle" key per sequence
-set to 4x the RMS-normalised weighted query sum, as in the planted-needle synthetic
-test of "The Hypothesis That Refused to Die" ("Message 12994: The Synthetic Test":
-a needle aligned with the query direction and scaled up).  Draw order from
-PCG64(seed) is fixed: centres, per-sequence centre indices then noise, q, w,
+set to 4x the RMS-normalised weighted query sum.  This mirrors the planted needle of
+"The Hypothesis That Refused to Die" ("Message 12994: The Synthetic Test"), a key
+pointing along the weighted query and several times longer than a filler key.
+Draw order from PCG64(seed) is fixed: centres, per-sequence centre indices then noise, q, w,
 needle depths, page-table permutation, then hidden states of newly stored tokens.
 Variable sequence lengths come from their own stream, PCG64(seed + 1).  Values are
 drawn in fp32 and rounded to bf16 (round to nearest even).

@@ -96,6 +96,12 @@ def test_q_prep_validation():
     assert call(out=None, codes=FAKE + 1, scales=FAKE) == dsa.IDX_EINVAL
     assert call(out=None, codes=FAKE, scales=FAKE + 2) == dsa.IDX_EINVAL
     assert call(dbg=FAKE + 4) == dsa.IDX_EINVAL
+    # the kernel moves 16-byte chunks of q, out_bf16 and prequant_dbg and 8-byte
+    # chunks of codes: those alignments are required
+    assert call(q=FAKE + 8) == dsa.IDX_EINVAL and "q_bf16" in err(lib)
+    assert call(out=FAKE + 8) == dsa.IDX_EINVAL and "out_bf16" in err(lib)
+    assert call(out=None, codes=FAKE + 4, scales=FAKE) == dsa.IDX_EINVAL and "codes" in err(lib)
+    assert call(dbg=FAKE + 8) == dsa.IDX_EINVAL and "prequant_dbg" in err(lib)
     # no RoPE: positions may be NULL; n = 0 is a no-op that never touches the GPU
     assert call(n=0, q=None, pos=None, flags=H) == dsa.IDX_OK
     assert err(lib) == ""
@@ -159,6 +165,25 @@ def test_topk_validation_and_workspace():
     assert "out_slots" in err(lib)
     assert lib.indexer_workspace_bytes(99, 4, 100, 8) == 0
     assert lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, 4, 100, 0) == 0
+
+
+def test_topk_plan_at_the_largest_sizes():
+    # the longest rows the ABI accepts need the most reduction levels (k = 8192 keeps
+    # half of each first-level chunk); the host-side plan must size them without
+    # overrunning its tables, and the workspace must cover two candidate lists of
+    # the first level's survivors
+    lib = dsa.load_library()
+    for rows, n, k in [(1, 2**31 - 1, 8192), (1, 2**31 - 1, 1), (3, 2**31 - 1, 4097),
+                       (65535, 2**31 - 1, 8192), (1, 36865, 8192), (1, 1 << 20, 8192)]:
+        need = lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, rows, n, k)
+        chunk0 = 16384
+        while chunk0 < 2 * k:
+            chunk0 *= 2
+        survivors = (n // chunk0) * min(k, chunk0) + min(n % chunk0, k)
+        assert need >= 2 * rows * survivors * 8, (rows, n, k, need)
+        assert need == lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, rows, n, k)   # deterministic
+        both = lib.indexer_workspace_bytes(dsa.IDX_OP_SCORE_TOPK, rows, n, k)
+        assert both == 0 or both > need
 
 
 def test_error_string_is_thread_local():

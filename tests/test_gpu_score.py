@@ -90,15 +90,17 @@ def test_rows_sharing_a_sequence():
     check_scores(got, oracle_scores(wl, OracleKeys(wl, "bf16")), wl.row_len, RTOL["bf16"])
 
 
+@pytest.mark.parametrize("bs", [64, 32])
 @pytest.mark.parametrize("case", ["bf16_keys", "fp8_keys", "fp8_prefill", "fp4_keys"])
-def test_bad_block_id_scores_nan_without_faulting(case):
-    # a block id outside the pool is caught by the kernel's bounds check: the keys
-    # it covers score NaN in every row that sees them, nothing is read out of bounds
+def test_bad_block_id_scores_nan_without_faulting(case, bs):
+    # a block id outside the pool is caught by the kernel's bounds check: exactly the
+    # keys it covers score NaN in every row that sees them (at block size 32 the
+    # other half of the 64-key span stays finite), nothing is read out of bounds
     # (one case per scoring kernel: bf16 keys, fp8 keys, fp8 queries, fp4 keys)
-    wl = {"bf16_keys": lambda: gen.config(1, scale=0.2),
-          "fp8_keys": lambda: gen.config(2, scale=0.05),
-          "fp8_prefill": lambda: gen.config(4, scale=0.02),
-          "fp4_keys": lambda: gen.config(3, scale=0.01)}[case]()
+    wl = {"bf16_keys": lambda: gen.config(1, scale=0.2, block_size=bs),
+          "fp8_keys": lambda: gen.config(2, scale=0.05, block_size=bs),
+          "fp8_prefill": lambda: gen.config(4, scale=0.02, block_size=bs),
+          "fp4_keys": lambda: gen.config(3, scale=0.01, block_size=bs)}[case]()
     seq = int(wl.row_seq[0])
     bt = wl.block_table.copy()
     bt[seq, 1] = wl.num_blocks + 5
@@ -116,6 +118,7 @@ def test_bad_block_id_scores_nan_without_faulting(case):
             continue
         assert np.all(np.isnan(got[r, bs:min(2 * bs, n)]))
         assert np.all(np.isfinite(got[r, :bs]))
+        assert np.all(np.isfinite(got[r, 2 * bs:n]))
         checked += 1
     assert checked > 0
 

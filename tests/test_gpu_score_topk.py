@@ -27,14 +27,45 @@ def fused(g: GpuWorkload, k=None, fp8_q=False):
     return out.cpu().numpy(), osc.cpu().numpy()
 
 
-def scores_of(g: GpuWorkload, fp8_q=False):
+def scores_dev(g: GpuWorkload, fp8_q=False):
     wl = g.wl
     out = torch.empty((wl.rows, wl.max_row_len), dtype=torch.float32, device="cuda")
     q, qs = g.query(fp8_q)
     note(f"indexer_score {wl.name} rows={wl.rows}")
     dsa.indexer_score(q, g.w, g.cache, g.rows, out, q_scale=qs)
     torch.cuda.synchronize()
+    return out
+
+
+def scores_of(g: GpuWorkload, fp8_q=False):
+    return scores_dev(g, fp8_q).cpu().numpy()
+
+
+def topk_of(g: GpuWorkload, scores, k=None):
+    """indexer_topk on device score rows [rows, ld] of the workload's rows."""
+    wl = g.wl
+    k = k or wl.k
+    out = torch.full((wl.rows, k), -7, dtype=torch.int32, device="cuda")
+    ws = dsa.alloc_workspace(dsa.IDX_OP_TOPK, wl.rows, wl.max_row_len, k)
+    note(f"indexer_topk {wl.name} on its own scores rows={wl.rows} k={k}")
+    dsa.indexer_topk(scores, g.row_len, wl.max_row_len, k, out, ws)
+    torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def check_topk_on_own_scores(g: GpuWorkload, scores, sel, rows=None):
+    """C3: the top-k of the GPU's own float32 score rows, standalone and inside the
+    fused call (which scores bit-identically), equals the oracle's sort-based top-k
+    of those same rows exactly."""
+    wl = g.wl
+    rows = np.arange(wl.rows) if rows is None else np.asarray(rows)
+    host = scores.cpu().numpy() if torch.is_tensor(scores) else scores
+    want = O.topk(host[rows], wl.row_len[rows], wl.k)
+    alone = topk_of(g, scores if torch.is_tensor(scores) else torch.from_numpy(host).cuda())
+    for i, r in enumerate(rows):
+        assert np.array_equal(alone[r], want[i]), (f"row {r}: indexer_topk differs from the oracle's top-k "
+                                                   f"of the same rows: {np.setdiff1d(alone[r], want[i])[:5]}")
+        assert np.array_equal(sel[r], want[i]), f"row {r}: fused selection differs from the oracle's top-k"
 
 
 CASES = [
@@ -78,7 +109,9 @@ def test_decode_b32_full_size():
     o = oracle_scores(wl, ok)
     st = check_selection(sel, o, wl.row_len, wl.k, RTOL["fp8"], slack=ok.slack())
     print(st)
-    check_scores(scores_of(g), o, wl.row_len, RTOL["fp8"], slack=ok.slack())
+    sd = scores_dev(g)
+    check_scores(sd.cpu().numpy(), o, wl.row_len, RTOL["fp8"], slack=ok.slack())
+    check_topk_on_own_scores(g, sd, sel)
     for r in range(wl.rows):
         assert wl.needle_pos[r] in set(sel[r].tolist())
 
@@ -117,6 +150,7 @@ def test_long_decode_b4_full_size():
     g = GpuWorkload(wl)
     g.store_new()
     sel, _ = fused(g)
+    check_topk_on_own_scores(g, scores_dev(g), sel)
     ok = OracleKeys(wl)
     o = oracle_scores(wl, ok)
     print(check_selection(sel, o, wl.row_len, wl.k, RTOL["fp8"], slack=ok.slack()))
@@ -135,3 +169,6 @@ def test_prefill_fused_selection(scale):
     rows = np.arange(wl.rows) if wl.rows <= 256 else np.linspace(0, wl.rows - 1, 48).astype(int)
     o = oracle_scores(wl, OracleKeys(wl), rows=rows, q64=q64[rows])
     print(check_selection(sel[rows], o, wl.row_len[rows], wl.k, RTOL["fp8"]))
+    # C3 on the GPU's own scores of the same rows (every row's top-k runs on the GPU)
+    sd = scores_dev(g, fp8_q=True)
+    check_topk_on_own_scores(g, sd, sel, rows=rows if wl.rows <= 256 else np.linspace(0, wl.rows - 1, 256).astype(int))

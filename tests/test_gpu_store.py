@@ -205,6 +205,12 @@ def test_store_chain_fp8(flags, base, rope_dim, posk):
     amax = np.abs(y64).max(axis=1, keepdims=True)
     assert np.all(np.abs(yg - y64) <= 1e-5 * amax), np.max(np.abs(yg - y64) / amax)
     gc, gs = read_fp8_cache(buf.cpu().numpy(), bs, slots)
+    # the quantiser on the kernel's own float32 rows: codes and scales bit-exact
+    pc, ps = O.quant_fp8(dbg.cpu().numpy())
+    bad = np.argwhere(gc != pc)
+    assert bad.size == 0, (bad[:5], gc[tuple(bad[0])], pc[tuple(bad[0])])
+    assert np.array_equal(gs.view(np.uint32), ps.view(np.uint32))
+    # end to end against the float64 chain
     oc, os_ = O.quant_fp8(y64.astype(np.float32))
     assert np.all(np.abs(gs.astype(np.float64) / os_ - 1) <= 1e-5)
     diff = gc != oc
@@ -229,9 +235,14 @@ def test_store_chain_bf16_cache():
                       7, 1e-6, 10000.0, 64, prequant_dbg=dbg)
     torch.cuda.synchronize()
     y64 = O.store_chain(bits, pos, 7, 1e-6, 10000.0, 64)
-    got = O.bf16_bits_to_f64(read_bf16_cache(buf.cpu().numpy(), bs, slots))
-    # one bf16 rounding of a value within 1e-5*amax of the exact one
+    yg = dbg.cpu().numpy()
     amax = np.abs(y64).max(axis=1, keepdims=True)
+    assert np.all(np.abs(yg.astype(np.float64) - y64) <= 1e-5 * amax)
+    cached = read_bf16_cache(buf.cpu().numpy(), bs, slots)
+    # the cache holds the nearest-even bf16 rounding of the kernel's own float32 rows
+    assert np.array_equal(cached, O.bf16_round(yg))
+    # and, end to end, one bf16 rounding of a value within 1e-5*amax of the exact one
+    got = O.bf16_bits_to_f64(cached)
     assert np.all(np.abs(got - y64) <= np.abs(y64) * 2.0 ** -8 + 1e-5 * amax)
 
 
@@ -244,3 +255,38 @@ def test_store_zero_tokens_is_noop():
                       dsa.kcache(buf, dsa.IDX_FP8_E4M3, 64, 1), dsa.IDX_STORE_ALL)
     torch.cuda.synchronize()
     assert torch.all(buf == 0)
+
+
+def test_store_encoder_on_a_large_float32_sample():
+    # The store converts y / s with the hardware e4m3 conversion after a +-448 clamp.
+    # Here 2^17 keys (16.8M quotients y / s) go through the chain: half normalised,
+    # rotated and rotary-embedded Gaussian rows, half rotary-embedded rows whose
+    # elements spread over 20 binades (so the quotients fill e4m3's subnormal range
+    # too).  The cache must hold quant_fp8 of the kernel's own float32 rows, bit for
+    # bit: every code is e4m3(RN32(y / s)) rounded to nearest even.
+    rng = np.random.default_rng(21)
+    n, bs = 1 << 17, 64
+    half = n // 2
+    a = rng.standard_normal((half, 128)) * rng.uniform(0.1, 10, (half, 1))
+    b = rng.standard_normal((half, 128)) * np.exp(rng.uniform(-14, 0, (half, 128)))
+    buf = torch.zeros((dsa.cache_bytes(dsa.IDX_FP8_E4M3, bs, n // bs),), dtype=torch.uint8, device="cuda")
+    cache = dsa.kcache(buf, dsa.IDX_FP8_E4M3, bs, n // bs)
+    dbg = torch.empty((n, 128), dtype=torch.float32, device="cuda")
+    slots = np.arange(n, dtype=np.int64)
+    for lo, x, flags in ((0, a, 7), (half, b, 2)):
+        bits = gen.f32_to_bf16_bits(x.astype(np.float32))
+        pos = rng.integers(0, 1 << 20, half).astype(np.int32)
+        note(f"index_k_store encoder sample flags={flags} n={half}")
+        dsa.index_k_store(bf16_tensor(bits), i32(pos), i64(slots[lo:lo + half]), cache, flags,
+                          1e-6, 10000.0, 64, prequant_dbg=dbg[lo:lo + half])
+    torch.cuda.synchronize()
+    y = dbg.cpu().numpy()
+    raw = buf.cpu().numpy().reshape(n // bs, bs * 132)
+    gc = raw[:, :bs * 128].reshape(n, 128)
+    gs = raw[:, bs * 128:].copy().view(np.float32).reshape(n)
+    pc, ps = O.quant_fp8(y)
+    assert np.array_equal(gs.view(np.uint32), ps.view(np.uint32))
+    bad = np.argwhere(gc != pc)
+    assert bad.size == 0, (bad.shape[0], bad[:5], y[tuple(bad[0])] / ps[bad[0][0]])
+    q = np.abs(y / ps[:, None])
+    assert np.sum((q > 0) & (q < 2.0 ** -6)) > 100_000      # the subnormal range was reached

@@ -149,3 +149,41 @@ def test_quant_dequant_error_within_half_step():
     e = np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6)))
     bound = np.exp2(e - 4) * (1 + 1e-6) + 1e-7 * np.abs(y)
     assert np.all(np.abs(d - y) <= bound)
+
+
+def test_bf16_decode_every_pattern_matches_torch():
+    # all 65,536 bf16 bit patterns against torch's own bfloat16 -> float64 conversion
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = O.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert nan.sum() == 2 * 127                 # exponent all ones, non-zero mantissa, both signs
+    assert np.array_equal(ours[~nan].view(np.uint64), ref[~nan].view(np.uint64))   # -0 kept
+    assert np.array_equal(O.bf16_bits_to_f32(bits)[~nan].astype(np.float64), ref[~nan])
+    # a few values fixed by the format: sign, 8 exponent bits (bias 127), 7 mantissa bits
+    assert ours[0x3F80] == 1.0 and ours[0xBF80] == -1.0 and ours[0x4049] == 3.140625
+    assert ours[0x0001] == 2.0 ** -133 and ours[0x7F7F] == (2 - 2.0 ** -7) * 2.0 ** 127
+    assert np.isinf(ours[0x7F80]) and ours[0xFF80] == -np.inf
+
+
+def test_bf16_round_matches_torch():
+    # torch's float32 -> bfloat16 conversion rounds to nearest even: every bf16
+    # midpoint and its float32 neighbours, plus random float32 over a wide range
+    rng = np.random.default_rng(11)
+    b = np.arange(0, 0x7F7F, dtype=np.uint32)                    # finite bf16 magnitudes
+    mids = ((b << 16) | 0x8000).view(np.float32)
+    cand = [mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf)),
+            ((b << 16)).view(np.float32),
+            (rng.standard_normal(1 << 18) * np.exp(rng.uniform(-80, 80, 1 << 18))).astype(np.float32)]
+    x = np.concatenate(cand).astype(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < np.float32(3.38e38))]
+    x = np.concatenate([x, -x])
+    ours = O.bf16_round(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bad = np.flatnonzero(ours != ref)
+    assert bad.size == 0, (x[bad[:5]], ours[bad[:5]], ref[bad[:5]])
+    # ties go to the even mantissa: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    assert O.bf16_round(np.float32(1 + 2.0 ** -8))[()] == 0x3F80
+    assert O.bf16_round(np.float32(1 + 3 * 2.0 ** -8))[()] == 0x3F82
+    assert O.bf16_round(np.float32(-0.0))[()] == 0x8000

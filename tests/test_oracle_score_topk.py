@@ -180,3 +180,33 @@ def test_jaccard_reproduces_printed_table():
 def test_jaccard_ignores_padding():
     assert O.jaccard([1, 2, -1], [2, 1, -1]) == (1.0, 0)
     assert O.jaccard([1, 2, 3, -1], [2, 5, -1, -1]) == (0.25, 2)
+
+
+# ---------------------------------------------------------------- threshold ------
+
+def test_kth_score_hand_worked_row_with_ties():
+    # descending order of the first 7 entries: 9, 7, 7, 7, 4, 1, -2 (the 8th entry is
+    # past the visible length and must not count)
+    row = np.array([7.0, 1.0, 9.0, 7.0, -2.0, 4.0, 7.0, 100.0])
+    n = 7
+    assert [O.kth_score(row, n, k) for k in range(1, 8)] == [9.0, 7.0, 7.0, 7.0, 4.0, 1.0, -2.0]
+    # k >= n: the smallest visible score
+    assert O.kth_score(row, n, 7) == O.kth_score(row, n, 8) == O.kth_score(row, n, 1000) == -2.0
+    # the threshold is the score of the last element the oracle's top-k keeps
+    for k in range(1, 8):
+        keep = O.topk(row[None], [n], k)[0][:k]
+        assert min(row[keep]) == O.kth_score(row, n, k)
+
+
+def test_kth_score_is_the_kth_order_statistic():
+    # against a counting definition: tau has >= k visible scores at or above it and
+    # fewer than k strictly above it
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        row = rng.integers(-4, 5, size=n + 3).astype(np.float64)
+        for k in range(1, n + 3):
+            t = O.kth_score(row, n, k)
+            vis = row[:n]
+            kk = min(k, n)
+            assert np.sum(vis >= t) >= kk and np.sum(vis > t) < kk
