@@ -105,6 +105,7 @@ def test_bad_block_id_scores_nan_without_faulting(case, bs):
     bt = wl.block_table.copy()
     bt[seq, 1] = wl.num_blocks + 5
     g = GpuWorkload(wl, block_table=bt, key_dtype="fp4" if case == "fp4_keys" else None)
+    g.store_new()   # (decode b32 keeps each sequence's newest key for the store chain)
     if case == "fp8_prefill":
         g.quantise_q()
         got = gpu_scores(g, fp8_q=True)
