@@ -15,7 +15,8 @@
  * ---------------------------------------
  *  - Pointers named as device buffers are device pointers owned by the caller.  The
  *    library never allocates or frees device memory, never synchronises a stream and
- *    never reads device data on the host.  Scratch space is the caller's `ws`.
+ *    never reads device data on the host.  Scratch space is the caller's `ws`
+ *    (indexer_score_topk_static alone uses a static array of the library instead).
  *  - All work is queued on `hip_stream` (a hipStream_t; NULL = the null stream) and
  *    is asynchronous.  No call records a memset, so calls can be captured in a HIP
  *    graph.
@@ -30,7 +31,8 @@
  *    [0, max_row_len] and a row_seq outside [0, num_seqs) scores NaN.
  *  - head_dim is 128 throughout.  Outputs are bit-deterministic: there are no
  *    floating-point atomics.
- *  - Calls are re-entrant; the only global state is the thread-local error string.
+ *  - Calls are re-entrant; the only global state is the thread-local error string
+ *    and the static scratch array of indexer_score_topk_static (one per GPU).
  */
 #ifndef DSA_INDEXER_H
 #define DSA_INDEXER_H
@@ -246,6 +248,26 @@ int32_t indexer_score_topk(const void* q, int32_t q_dtype, const float* q_scale,
                            int32_t heads, idx_kcache cache, idx_rows rows, int32_t k,
                            int32_t* out_idx, int64_t* out_slots, float* out_scores, void* ws,
                            size_t ws_bytes, void* hip_stream);
+
+/*
+ * indexer_score_topk_static - indexer_score_topk for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results as indexer_score_topk, without ws:
+ * the score rows and candidate lists live in a static device array of
+ * IDX_STATIC_SCRATCH_BYTES per GPU, which the library holds from the first call on
+ * that GPU until the process ends.  The call allocates and frees nothing.
+ *   Limit: indexer_workspace_bytes(IDX_OP_SCORE_TOPK, rows, max_row_len, k) must not
+ *   exceed IDX_STATIC_SCRATCH_BYTES (e.g. 32 rows of up to ~200k keys, or 4 rows of
+ *   1M keys at k = 1024); larger calls return IDX_EWORKSPACE and launch nothing.
+ *   Sharing: every call on one GPU uses that GPU's one array, and nothing in it needs
+ *   to start at zero, but calls that overlap in time on one GPU (different streams,
+ *   or host threads without ordering) race on it and must be serialised by the caller.
+ */
+#define IDX_STATIC_SCRATCH_BYTES (32u << 20)
+int32_t indexer_score_topk_static(const void* q, int32_t q_dtype, const float* q_scale,
+                                  const float* w, int32_t heads, idx_kcache cache, idx_rows rows,
+                                  int32_t k, int32_t* out_idx, int64_t* out_slots,
+                                  float* out_scores, void* hip_stream);
 
 /*
  * indexer_translate - selected logical key positions -> physical cache slots (the

@@ -18,11 +18,12 @@ IDX_BF16, IDX_FP8_E4M3, IDX_MXFP4 = 1, 2, 3
 IDX_STORE_RMSNORM, IDX_STORE_ROPE, IDX_STORE_HADAMARD = 1, 2, 4
 IDX_STORE_ALL = 7
 IDX_OP_TOPK, IDX_OP_SCORE_TOPK = 1, 2
+IDX_STATIC_SCRATCH_BYTES = 32 << 20
 HEAD_DIM = 128
 
 EXPORTED = ("index_k_store", "indexer_q_prep", "indexer_quant_fp8", "indexer_score", "indexer_topk",
-            "indexer_score_topk", "indexer_translate", "indexer_workspace_bytes", "indexer_last_error",
-            "indexer_abi_version")
+            "indexer_score_topk", "indexer_score_topk_static", "indexer_translate",
+            "indexer_workspace_bytes", "indexer_last_error", "indexer_abi_version")
 
 
 class IndexerError(RuntimeError):
@@ -67,6 +68,7 @@ def load_library(path: str = LIB_PATH):
         "indexer_score": (i32, [vp, i32, vp, vp, i32, KCache, Rows, vp, i64, vp]),
         "indexer_topk": (i32, [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]),
         "indexer_score_topk": (i32, [vp, i32, vp, vp, i32, KCache, Rows, i32, vp, vp, vp, vp, sz, vp]),
+        "indexer_score_topk_static": (i32, [vp, i32, vp, vp, i32, KCache, Rows, i32, vp, vp, vp, vp]),
         "indexer_translate": (i32, [vp, i64, i32, KCache, Rows, vp, i64, vp]),
         "indexer_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "indexer_last_error": (ctypes.c_char_p, []),
@@ -245,6 +247,22 @@ def indexer_score_topk(q, w, cache: KCache, rows: Rows, k: int, out_idx, ws, out
     _check("indexer_score_topk", load_library().indexer_score_topk(
         _ptr(q), q_dtype, _ptr(q_scale), _ptr(w), heads, cache, rows, k, _ptr(out_idx),
         _ptr(out_slots), _ptr(out_scores), _ptr(ws), nbytes, _stream(stream)))
+
+
+def indexer_score_topk_static(q, w, cache: KCache, rows: Rows, k: int, out_idx, out_scores=None,
+                              q_scale=None, out_slots=None, stream=None):
+    """indexer_score_topk with the library's static per-GPU scratch instead of a
+    workspace (nothing is allocated; overlapping calls on one GPU race)."""
+    import torch
+    q_dtype, heads = _q_args(q, q_scale, w)
+    _need(out_idx, torch.int32, "out_idx")
+    _need(out_scores, torch.float32, "out_scores")
+    _need(out_slots, torch.int64, "out_slots")
+    if out_slots is not None and out_slots.numel() < out_idx.numel():
+        raise ValueError("out_slots must hold [rows, k] entries")
+    _check("indexer_score_topk_static", load_library().indexer_score_topk_static(
+        _ptr(q), q_dtype, _ptr(q_scale), _ptr(w), heads, cache, rows, k, _ptr(out_idx),
+        _ptr(out_slots), _ptr(out_scores), _stream(stream)))
 
 
 def indexer_translate(idx, cache: KCache, rows: Rows, out_slots, stream=None):

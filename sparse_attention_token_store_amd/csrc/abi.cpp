@@ -7,10 +7,17 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dsa_indexer.h"
 #include "launch.hpp"
+
+// Workspace of indexer_score_topk_static: one copy per GPU, from the moment the
+// library's code object is loaded on that GPU until the process ends.  On the host
+// this name is only a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[IDX_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -98,6 +105,37 @@ int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 int64_t score_ld(int32_t max_row_len) { return round_up(max_row_len > 0 ? max_row_len : 1, 64); }
 size_t score_bytes(int32_t rows, int32_t max_row_len) {
   return (size_t)round_up((int64_t)rows * score_ld(max_row_len) * 4, 256);
+}
+
+// Device address of `scratch` on the GPU that owns `s` (the current device for the
+// null stream), looked up once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_of_stream(hipStream_t s, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(IDX_ELAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  dev = cur;
+  if (s) {
+    e = hipStreamGetDevice(s, &dev);
+    if (e != hipSuccess) return fail(IDX_ELAUNCH, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(IDX_EUNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(IDX_ELAUNCH, "hipSetDevice(%d) failed: %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p)
+      return fail(IDX_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return IDX_OK;
 }
 
 }  // namespace
@@ -251,22 +289,24 @@ IDX_API int32_t indexer_topk(const float* scores, int64_t ld, const int32_t* row
                   "indexer_topk");
 }
 
-IDX_API int32_t indexer_score_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
-                           int32_t heads, idx_kcache cache, idx_rows rows, int32_t k, int32_t* out_idx,
-                           int64_t* out_slots, float* out_scores, void* ws, size_t ws_bytes,
-                           void* hip_stream) {
-  g_err.clear();
+static int32_t check_score_topk_args(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                                     int32_t heads, const idx_kcache& cache, const idx_rows& rows, int32_t k,
+                                     int32_t* out_idx, int64_t* out_slots, float* out_scores) {
   if (int32_t e = check_score_args(q, q_dtype, q_scale, w, heads, cache, rows)) return e;
   if (int32_t e = check_topk_common(rows.rows, rows.max_row_len, k, out_idx)) return e;
   if (out_slots && !aligned(out_slots, 8)) return fail(IDX_EINVAL, "out_slots must be 8-byte aligned");
   if (out_scores && !aligned(out_scores, 4)) return fail(IDX_EINVAL, "out_scores must be 4-byte aligned");
-  if (rows.rows == 0) return IDX_OK;
-  const size_t need = score_bytes(rows.rows, rows.max_row_len) +
-                      dsa::topk_ws_bytes(rows.rows, rows.max_row_len, k);
-  if (!ws || ws_bytes < need)
-    return fail(IDX_EWORKSPACE, "workspace of %zu bytes required, %zu given", need, ws ? ws_bytes : (size_t)0);
-  if (!aligned(ws, 256)) return fail(IDX_EINVAL, "ws must be 256-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  return IDX_OK;
+}
+
+static size_t score_topk_ws_bytes(int32_t rows, int32_t max_row_len, int32_t k) {
+  return score_bytes(rows, max_row_len) + dsa::topk_ws_bytes(rows, max_row_len, k);
+}
+
+// The score rows go to the start of ws, the top-k lists after them.
+static int32_t run_score_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                              const idx_kcache& cache, const idx_rows& rows, int32_t k, int32_t* out_idx,
+                              int64_t* out_slots, float* out_scores, void* ws, hipStream_t s, const char* who) {
   float* sc = static_cast<float*>(ws);
   const int64_t ld = score_ld(rows.max_row_len);
   if (rows.max_row_len > 0)
@@ -274,7 +314,44 @@ IDX_API int32_t indexer_score_topk(const void* q, int32_t q_dtype, const float* 
   void* tws = static_cast<uint8_t*>(ws) + score_bytes(rows.rows, rows.max_row_len);
   return launched(dsa::launch_topk(sc, ld, rows.row_len, rows.rows, rows.max_row_len, k, out_idx,
                                    out_scores, to_map(cache, rows, out_slots, k), tws, s),
-                  "indexer_score_topk");
+                  who);
+}
+
+IDX_API int32_t indexer_score_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                           int32_t heads, idx_kcache cache, idx_rows rows, int32_t k, int32_t* out_idx,
+                           int64_t* out_slots, float* out_scores, void* ws, size_t ws_bytes,
+                           void* hip_stream) {
+  g_err.clear();
+  if (int32_t e = check_score_topk_args(q, q_dtype, q_scale, w, heads, cache, rows, k, out_idx, out_slots,
+                                        out_scores))
+    return e;
+  if (rows.rows == 0) return IDX_OK;
+  const size_t need = score_topk_ws_bytes(rows.rows, rows.max_row_len, k);
+  if (!ws || ws_bytes < need)
+    return fail(IDX_EWORKSPACE, "workspace of %zu bytes required, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if (!aligned(ws, 256)) return fail(IDX_EINVAL, "ws must be 256-byte aligned");
+  return run_score_topk(q, q_dtype, q_scale, w, cache, rows, k, out_idx, out_slots, out_scores, ws,
+                        static_cast<hipStream_t>(hip_stream), "indexer_score_topk");
+}
+
+IDX_API int32_t indexer_score_topk_static(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                                          int32_t heads, idx_kcache cache, idx_rows rows, int32_t k,
+                                          int32_t* out_idx, int64_t* out_slots, float* out_scores,
+                                          void* hip_stream) {
+  g_err.clear();
+  if (int32_t e = check_score_topk_args(q, q_dtype, q_scale, w, heads, cache, rows, k, out_idx, out_slots,
+                                        out_scores))
+    return e;
+  if (rows.rows == 0) return IDX_OK;
+  const size_t need = score_topk_ws_bytes(rows.rows, rows.max_row_len, k);
+  if (need > (size_t)IDX_STATIC_SCRATCH_BYTES)
+    return fail(IDX_EWORKSPACE, "needs %zu bytes of scratch; the static scratch holds %zu (use indexer_score_topk "
+                "with a workspace)", need, (size_t)IDX_STATIC_SCRATCH_BYTES);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  void* ws = nullptr;
+  if (int32_t e = scratch_of_stream(s, &ws)) return e;
+  return run_score_topk(q, q_dtype, q_scale, w, cache, rows, k, out_idx, out_slots, out_scores, ws, s,
+                        "indexer_score_topk_static");
 }
 
 IDX_API int32_t indexer_translate(const int32_t* idx, int64_t ld_idx, int32_t k, idx_kcache cache,

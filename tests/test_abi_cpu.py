@@ -227,3 +227,27 @@ def test_translate_validation():
     # nothing to do: no launch, no pointer needed
     assert call(k=0, idx=None, slots=None) == dsa.IDX_OK
     assert call(rows=rows(n=0), idx=None, slots=None) == dsa.IDX_OK
+
+
+def test_static_scratch_entry_point_validation():
+    # the allocation-free variant runs the same argument checks as indexer_score_topk
+    # and refuses, before touching the GPU, any call whose workspace would not fit the
+    # static scratch array
+    lib = dsa.load_library()
+    f = lib.indexer_score_topk_static
+    assert f(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 0, FAKE, None, None, None) == dsa.IDX_EINVAL
+    assert f(FAKE, dsa.IDX_BF16, None, FAKE, 32, cache(), rows(), 8, FAKE, None, None, None) == dsa.IDX_EUNSUPPORTED
+    assert f(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(), 8, FAKE, FAKE + 4, None, None) == dsa.IDX_EINVAL
+    assert f(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(), rows(n=0), 8, FAKE, None, None, None) == dsa.IDX_OK
+    # 16 rows of 1M keys need ~70 MB of scores: more than the 32 MiB the array holds
+    big = dsa.Rows(FAKE, 1 << 14, 16, FAKE, FAKE, 16, 1 << 20)
+    need = lib.indexer_workspace_bytes(dsa.IDX_OP_SCORE_TOPK, 16, 1 << 20, 1024)
+    assert need > dsa.IDX_STATIC_SCRATCH_BYTES
+    assert f(FAKE, dsa.IDX_BF16, None, FAKE, 64, cache(nb=1 << 18), big, 1024, FAKE, None, None, None) == \
+        dsa.IDX_EWORKSPACE
+    assert "static scratch" in err(lib) and str(dsa.IDX_STATIC_SCRATCH_BYTES) in err(lib)
+    # the long-decode and decode-batch shapes fit
+    assert lib.indexer_workspace_bytes(dsa.IDX_OP_SCORE_TOPK, 4, 1 << 20, 1024) <= dsa.IDX_STATIC_SCRATCH_BYTES
+    assert lib.indexer_workspace_bytes(dsa.IDX_OP_SCORE_TOPK, 32, 22000, 512) <= dsa.IDX_STATIC_SCRATCH_BYTES
+    header = open(HEADER).read()
+    assert re.search(r"#define IDX_STATIC_SCRATCH_BYTES \(32u << 20\)", header)
