@@ -51,6 +51,12 @@ tests/test_oracle_*.py):
                                              injectivity on a shuffled table)
   jaccard .................................. pinned (the printed table of the
                                              synthetic fp8-vs-bf16 test)
+  sparse_attention, merge_attention ....... pinned (torch's scaled-dot-product
+                                             attention in float64, closed forms for
+                                             one slot and for a zero query, dense
+                                             attention when every slot is listed,
+                                             permutation invariance, the merge
+                                             identity over disjoint sets)
 """
 from __future__ import annotations
 
@@ -513,3 +519,73 @@ def jaccard(a, b) -> tuple[float, int]:
     if not union:
         return 1.0, 0
     return len(sa & sb) / len(union), len(sa - sb)
+
+
+# ----------------------------------------------------------------------------------
+# Sparse attention over the selections (the consumer of the top-k)
+# ----------------------------------------------------------------------------------
+#
+# The pages place the selections' consumer beside the indexer without printing it:
+# the decode attention kernel reads the rows the indexer selected, after the logical
+# -> physical translation ([ATOM-1507] "How it was isolated": the decode attention
+# kernel and csa_translate_pack each checked on their own; "Root cause found": a
+# key the indexer drops is invisible to sparse attention while dense attention,
+# which reads every row, still sees it).  The main KV cache holds one compressed
+# KV state per token of head_dim 512 ([PIVOT-EDIT] "Assumptions and Input
+# Knowledge": head_dim 512 for the main KV against 128 for the indexer; the
+# compressor stores compressed KV states).
+#
+# READING: multi-query latent attention in its absorbed form, the plainest one the
+# pages support: every query head attends over the same per-token 512-dim state,
+# which serves as key and as value; the score is a scaled dot product and the
+# softmax runs over the listed (selected) slots only.  The log-sum-exp of each
+# head's scores is returned too, so that attention over two disjoint sets (the
+# sparse selection and, say, a sliding window of recent tokens, the pages' two KV
+# paths) merges exactly (merge_attention below).
+
+
+def sparse_attention(q: np.ndarray, kv: np.ndarray, slots: np.ndarray, scale: float):
+    """float64 attention of every query head over the KV rows a row lists.
+
+    q: [rows, H, D] query heads; kv: [num_slots, D] KV states (float64, already
+    decoded); slots: [rows, k] integer slot lists, negative entries are padding.
+    For row r with listed slots p_1..p_n (n >= 1; repeated slots count as often as
+    they are listed), and each head h:
+        s_j   = scale * q[r, h] . kv[p_j]
+        o     = sum_j exp(s_j - m) kv[p_j] / sum_j exp(s_j - m),   m = max_j s_j
+        lse   = m + log(sum_j exp(s_j - m))                (= log sum_j exp s_j)
+    A row with no listed slot gives o = 0 and lse = -inf.
+    Returns (o float64 [rows, H, D], lse float64 [rows, H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    slots = np.asarray(slots)
+    rows, H, D = q.shape
+    out = np.zeros((rows, H, D), dtype=np.float64)
+    lse = np.full((rows, H), -np.inf, dtype=np.float64)
+    for r in range(rows):
+        sel = slots[r][slots[r] >= 0].astype(np.int64)
+        if sel.size == 0:
+            continue
+        x = kv[sel]                                   # [n, D]
+        s = float(scale) * (q[r] @ x.T)               # [H, n]
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        z = e.sum(axis=1, keepdims=True)
+        out[r] = (e @ x) / z
+        lse[r] = (m + np.log(z))[:, 0]
+    return out, lse
+
+
+def merge_attention(o1, lse1, o2, lse2):
+    """Attention over the union of two disjoint slot sets from each set's output and
+    log-sum-exp: weights exp(lse_i - lse) with lse = log(exp lse1 + exp lse2)."""
+    o1, o2 = np.asarray(o1, np.float64), np.asarray(o2, np.float64)
+    lse1, lse2 = np.asarray(lse1, np.float64), np.asarray(lse2, np.float64)
+    m = np.maximum(lse1, lse2)
+    safe = np.where(np.isfinite(m), m, 0.0)
+    w1, w2 = np.exp(lse1 - safe), np.exp(lse2 - safe)
+    z = w1 + w2
+    lse = np.where(np.isfinite(m), safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+    zz = np.where(z > 0, z, 1.0)[..., None]
+    return (w1[..., None] * o1 + w2[..., None] * o2) / zz, lse
