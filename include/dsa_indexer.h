@@ -286,6 +286,42 @@ int32_t indexer_score_topk_static(const void* q, int32_t q_dtype, const float* q
 int32_t indexer_translate(const int32_t* idx, int64_t ld_idx, int32_t k, idx_kcache cache,
                           idx_rows rows, int64_t* slots, int64_t ld_slots, void* hip_stream);
 
+/*
+ * indexer_sparse_attention - decode attention of every query head over the KV
+ * states of its row's selected slots only (the consumer of the selections:
+ * [ATOM-1507] "How it was isolated" checks the decode attention kernel after the
+ * logical -> physical translation; "Root cause found": a key the selection drops is
+ * invisible to sparse attention).  The main KV cache holds one compressed KV state
+ * of head_dim 512 per token ([PIVOT-EDIT] "Assumptions and Input Knowledge"), which
+ * serves as key and value for every head (multi-query latent attention, absorbed
+ * form).  For row r, head h and the listed slots s_1..s_n (entries < 0 skipped):
+ *     x_j = scale * q[r][h] . kv[s_j]
+ *     out[r][h] = sum_j exp(x_j - m) kv[s_j] / sum_j exp(x_j - m),  m = max_j x_j
+ *     lse[r][h] = log sum_j exp(x_j)          (so disjoint sets merge exactly)
+ * A row that lists nothing gets out = 0 and lse = -inf; a listed slot >= num_slots
+ * is never read and makes its row's out and lse NaN.  Scores and sums are fp32;
+ * the probabilities meet the KV states in bf16 (MFMA) with fp32 accumulation.
+ *   q          device bf16 [rows][heads][512].
+ *   heads      16, 32, 64 or 128 query heads.
+ *   kv         device bf16 [num_slots][512]: slot s = block*block_size + offset of
+ *              a paged cache with 512*2-byte tokens (any block size), 16-byte aligned.
+ *   slots      device int64 [rows][ld_slots]: the first k entries of each row are
+ *              its list (indexer_score_topk's out_slots or indexer_translate's).
+ *   k          0 .. 65536.  scale  finite, > 0 (e.g. 1/sqrt(512)).
+ *   out        device fp32 [rows][heads][512], 16-byte aligned.
+ *   lse        NULL or device fp32 [rows][heads].
+ *   ws         indexer_attention_workspace_bytes(rows, k, heads) bytes (0: may be
+ *              NULL), 256-byte aligned: per-split partial results.
+ */
+int32_t indexer_sparse_attention(const void* q, int32_t heads, const void* kv, int64_t num_slots,
+                                 const int64_t* slots, int64_t ld_slots, int32_t k, int32_t rows,
+                                 float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                                 void* hip_stream);
+
+/* Workspace bytes of indexer_sparse_attention (0 when none is needed, or on bad
+ * arguments). */
+size_t indexer_attention_workspace_bytes(int32_t rows, int32_t k, int32_t heads);
+
 /* Workspace bytes needed by an op (IDX_OP_TOPK or IDX_OP_SCORE_TOPK); 0 on bad
  * arguments. */
 size_t indexer_workspace_bytes(int32_t op, int32_t rows, int32_t max_row_len, int32_t k);

@@ -23,7 +23,9 @@ HEAD_DIM = 128
 
 EXPORTED = ("index_k_store", "indexer_q_prep", "indexer_quant_fp8", "indexer_score", "indexer_topk",
             "indexer_score_topk", "indexer_score_topk_static", "indexer_translate",
+            "indexer_sparse_attention", "indexer_attention_workspace_bytes",
             "indexer_workspace_bytes", "indexer_last_error", "indexer_abi_version")
+KV_DIM = 512
 
 
 class IndexerError(RuntimeError):
@@ -70,6 +72,8 @@ def load_library(path: str = LIB_PATH):
         "indexer_score_topk": (i32, [vp, i32, vp, vp, i32, KCache, Rows, i32, vp, vp, vp, vp, sz, vp]),
         "indexer_score_topk_static": (i32, [vp, i32, vp, vp, i32, KCache, Rows, i32, vp, vp, vp, vp]),
         "indexer_translate": (i32, [vp, i64, i32, KCache, Rows, vp, i64, vp]),
+        "indexer_sparse_attention": (i32, [vp, i32, vp, i64, vp, i64, i32, i32, f32, vp, vp, vp, sz, vp]),
+        "indexer_attention_workspace_bytes": (sz, [i32, i32, i32]),
         "indexer_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "indexer_last_error": (ctypes.c_char_p, []),
         "indexer_abi_version": (i32, []),
@@ -278,12 +282,50 @@ def indexer_translate(idx, cache: KCache, rows: Rows, out_slots, stream=None):
         _stream(stream)))
 
 
-def alloc_workspace(op: int, rows: int, max_row_len: int, k: int, device="cuda"):
-    """A 256-byte aligned uint8 workspace tensor of the size the op needs (or None)."""
+def indexer_sparse_attention(q, kv, slots, out, k=None, scale=None, lse=None, ws=None, stream=None):
+    """q: bf16 [rows, heads, 512]; kv: bf16 [num_slots, 512] (the main KV cache seen
+    as slots); slots: int64 [rows, ld] (the first k entries of a row are its list,
+    negative entries padding); out: fp32 [rows, heads, 512]; lse: optional fp32
+    [rows, heads]; scale defaults to 1/sqrt(512); ws: alloc_attention_workspace()."""
     import torch
-    n = workspace_bytes(op, rows, max_row_len, k)
+    _need(q, torch.bfloat16, "q")
+    _need(kv, torch.bfloat16, "kv")
+    _need(slots, torch.int64, "slots")
+    _need(out, torch.float32, "out")
+    _need(lse, torch.float32, "lse")
+    if q.dim() != 3 or q.shape[-1] != KV_DIM or kv.dim() != 2 or kv.shape[-1] != KV_DIM:
+        raise ValueError("q must be [rows, heads, 512] and kv [num_slots, 512]")
+    rows, heads = q.shape[0], q.shape[1]
+    if slots.dim() != 2 or slots.shape[0] != rows or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("slots must be [rows, ld] and out [rows, heads, 512]")
+    if lse is not None and tuple(lse.shape) != (rows, heads):
+        raise ValueError("lse must be [rows, heads]")
+    k = slots.shape[1] if k is None else int(k)
+    scale = KV_DIM ** -0.5 if scale is None else float(scale)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("indexer_sparse_attention", load_library().indexer_sparse_attention(
+        _ptr(q), heads, _ptr(kv), kv.shape[0], _ptr(slots), slots.shape[1], k, rows, scale, _ptr(out),
+        _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
+
+
+def attention_workspace_bytes(rows: int, k: int, heads: int) -> int:
+    return int(load_library().indexer_attention_workspace_bytes(rows, k, heads))
+
+
+def _aligned_bytes(n: int, device):
+    import torch
     if n == 0:
         return None
     t = torch.empty(n + 256, dtype=torch.uint8, device=device)
     off = (-t.data_ptr()) % 256
     return t[off:off + n]
+
+
+def alloc_attention_workspace(rows: int, k: int, heads: int, device="cuda"):
+    """A 256-byte aligned workspace for indexer_sparse_attention (or None)."""
+    return _aligned_bytes(attention_workspace_bytes(rows, k, heads), device)
+
+
+def alloc_workspace(op: int, rows: int, max_row_len: int, k: int, device="cuda"):
+    """A 256-byte aligned uint8 workspace tensor of the size the op needs (or None)."""
+    return _aligned_bytes(workspace_bytes(op, rows, max_row_len, k), device)

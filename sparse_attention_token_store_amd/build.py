@@ -21,7 +21,7 @@ OUT = os.path.join(PKG, "libdsa_indexer.so")
 BENCH_OUT = os.path.join(PKG, "libdsa_bench.so")       # measurement kernels of bench.py
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.cpp", "store.hip", "score_decode.hip", "score_prefill.hip", "topk.hip"]
+SOURCES = ["abi.cpp", "store.hip", "score_decode.hip", "score_prefill.hip", "topk.hip", "attention.hip"]
 BENCH_SOURCES = ["bench_peaks.hip"]
 
 FLAGS = [

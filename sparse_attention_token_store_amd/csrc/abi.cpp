@@ -38,6 +38,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr int32_t kMaxK = 8192;
 constexpr int32_t kMaxRows = 65535;       // grid y dimension
 constexpr int32_t kHeadsV1 = 64;
+constexpr int32_t kMaxAttnK = 1 << 16;    // listed slots per attention row
 
 int32_t check_cache(const idx_kcache& c) {
   if (!c.base) return fail(IDX_EINVAL, "cache.base is NULL");
@@ -352,6 +353,40 @@ IDX_API int32_t indexer_score_topk_static(const void* q, int32_t q_dtype, const 
   if (int32_t e = scratch_of_stream(s, &ws)) return e;
   return run_score_topk(q, q_dtype, q_scale, w, cache, rows, k, out_idx, out_slots, out_scores, ws, s,
                         "indexer_score_topk_static");
+}
+
+IDX_API size_t indexer_attention_workspace_bytes(int32_t rows, int32_t k, int32_t heads) {
+  if (rows < 0 || rows > kMaxRows || k < 0 || k > kMaxAttnK) return 0;
+  if (heads != 16 && heads != 32 && heads != 64 && heads != 128) return 0;
+  return dsa::attention_ws_bytes(rows, k, heads);
+}
+
+IDX_API int32_t indexer_sparse_attention(const void* q, int32_t heads, const void* kv, int64_t num_slots,
+                                         const int64_t* slots, int64_t ld_slots, int32_t k, int32_t rows,
+                                         float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                                         void* hip_stream) {
+  g_err.clear();
+  if (heads != 16 && heads != 32 && heads != 64 && heads != 128)
+    return fail(IDX_EUNSUPPORTED, "heads=%d unsupported (16, 32, 64 or 128)", heads);
+  if (rows < 0 || rows > kMaxRows) return fail(IDX_EINVAL, "rows %d out of [0, %d]", rows, kMaxRows);
+  if (k < 0 || k > kMaxAttnK) return fail(IDX_EINVAL, "k=%d out of [0, %d]", k, kMaxAttnK);
+  if (ld_slots < k) return fail(IDX_EINVAL, "ld_slots %lld < k %d", (long long)ld_slots, k);
+  if (num_slots < 1 || num_slots > (int64_t)INT32_MAX) return fail(IDX_EINVAL, "num_slots must be in [1, INT32_MAX]");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(IDX_EINVAL, "scale must be finite and > 0");
+  if (rows == 0) return IDX_OK;
+  if (!q || !kv || !out || (k > 0 && !slots)) return fail(IDX_EINVAL, "q, kv, slots and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16))
+    return fail(IDX_EINVAL, "q, kv and out must be 16-byte aligned");
+  if (slots && !aligned(slots, 8)) return fail(IDX_EINVAL, "slots must be 8-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(IDX_EINVAL, "lse must be 4-byte aligned");
+  const size_t need = dsa::attention_ws_bytes(rows, k, heads);
+  if (need && (!ws || ws_bytes < need))
+    return fail(IDX_EWORKSPACE, "workspace of %zu bytes required, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if (need && !aligned(ws, 256)) return fail(IDX_EINVAL, "ws must be 256-byte aligned");
+  return launched(dsa::launch_attention(static_cast<const uint16_t*>(q), heads, static_cast<const uint8_t*>(kv),
+                                        num_slots, slots, ld_slots, k, rows, scale, out, lse, ws,
+                                        static_cast<hipStream_t>(hip_stream)),
+                  "indexer_sparse_attention");
 }
 
 IDX_API int32_t indexer_translate(const int32_t* idx, int64_t ld_idx, int32_t k, idx_kcache cache,

@@ -73,4 +73,11 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_len, 
 hipError_t launch_translate(const int32_t* idx, int64_t ld_idx, int rows, int k, const SlotMap& map,
                             hipStream_t s);
 
+// sparse attention of bf16 query heads [rows][heads][512] over the listed slots of a
+// bf16 KV array [num_slots][512]; ws of attention_ws_bytes(rows, k, heads) bytes
+size_t attention_ws_bytes(int rows, int k, int heads);
+hipError_t launch_attention(const uint16_t* q, int heads, const uint8_t* kv, int64_t num_slots, const int64_t* slots,
+                            int64_t ld, int k, int rows, float scale, float* out, float* lse, void* ws,
+                            hipStream_t s);
+
 }  // namespace dsa

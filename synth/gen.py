@@ -264,3 +264,34 @@ def score_rows_for_topk(rows: int, n: int, *, kind: str = "normal", seed: int = 
     else:
         raise ValueError(kind)
     return np.ascontiguousarray(x, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------------
+# Inputs of the sparse attention over the selections: query heads and one 512-dim
+# compressed KV state per token slot (drawn, not derived: the pages give neither).
+# ----------------------------------------------------------------------------------
+
+KV_DIM = 512
+
+
+def kv_states(num_slots: int, *, seed: int = 0, sd: float = 1.0) -> np.ndarray:
+    """bf16 bits [num_slots, 512]: N(0, sd^2) per element (own stream, PCG64(seed + 7))."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7))
+    return f32_to_bf16_bits((rng.standard_normal((num_slots, KV_DIM), dtype=np.float32) * np.float32(sd)))
+
+
+def attention_case(rows: int, heads: int, k: int, num_slots: int, *, pad_frac: float = 0.0,
+                   seed: int = 0, q_sd: float = 1.0):
+    """Query heads (bf16 bits [rows, heads, 512], N(0, q_sd^2)) and slot lists (int64
+    [rows, k]: distinct slots per row, min(k, num_slots) of them, drawn from
+    [0, num_slots); a fraction pad_frac of the entries set to -1 padding, -1 also past
+    num_slots)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = f32_to_bf16_bits(rng.standard_normal((rows, heads, KV_DIM), dtype=np.float32) * np.float32(q_sd))
+    slots = np.full((rows, k), -1, dtype=np.int64)
+    for r in range(rows):
+        m = min(k, num_slots)
+        slots[r, :m] = rng.choice(num_slots, m, replace=False)
+    if pad_frac > 0:
+        slots[rng.random((rows, k)) < pad_frac] = -1
+    return q, slots
