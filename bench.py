@@ -361,6 +361,55 @@ def bench_q_prep(args, run):
     }
 
 
+def bench_attention(probes, steps, warmup, heads, rows=32, k=512, num_slots=423936, lists=64):
+    """indexer_sparse_attention of `heads` query heads over `k` selected slots per row
+    (decode batch 32 at top-512: the slot space of the decode-batch KV cache, 512-dim
+    bf16 states, 434 MB), each step with a fresh list of distinct random slots (64
+    lists rotate, 1 GB of KV rows touched, so the gathers come from HBM).  Queued
+    ahead behind a device delay; fence-free events bracket the timed launches."""
+    import torch
+    import sparse_attention_token_store_amd as dsa
+    from synth import gen
+    rng = np.random.default_rng(1)
+    gen_t = torch.Generator(device="cuda").manual_seed(3)
+    kv = torch.randn((num_slots, 512), dtype=torch.bfloat16, device="cuda", generator=gen_t)
+    q_bits, _ = gen.attention_case(rows, heads, 1, 1, seed=2)
+    q = torch.from_numpy(q_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    sl = torch.from_numpy(np.stack([np.stack([rng.choice(num_slots, k, replace=False) for _ in range(rows)])
+                                    for _ in range(lists)]).astype(np.int64)).cuda()
+    out = torch.empty((rows, heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((rows, heads), dtype=torch.float32, device="cuda")
+    ws = dsa.alloc_attention_workspace(rows, k, heads)
+
+    def launch(i):
+        dsa.indexer_sparse_attention(q, kv, sl[i % lists], out, lse=lse, ws=ws)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    a, b = probes.event(), probes.event()
+    probes.spin(min(200_000.0, 2000.0 + 100.0 * steps))
+    a.record()
+    for i in range(steps):
+        launch(warmup + i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.ms_to(b) / steps
+    nbytes = rows * k * 1024 + rows * heads * 1024 + rows * heads * (512 * 4 + 4) + rows * k * 8
+    achieved = nbytes / (ms / 1e3) / 1e9
+    splits_ws = dsa.attention_workspace_bytes(rows, k, heads)
+    del kv, sl
+    torch.cuda.empty_cache()
+    return {"workload": f"sparse attention, {rows} rows x top-{k} slots, {heads} heads x 512, bf16 KV",
+            "ms_per_launch": ms, "rows_per_s": rows / (ms / 1e3),
+            "kv_rows_per_s": rows * k / (ms / 1e3), "heads": heads, "rows": rows, "k": k,
+            "split_workspace_bytes": splits_ws,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "algorithmic_per_launch": nbytes,
+                         "algorithmic_per_unit": "1024 B per listed KV row + 8 B slot; per row and head "
+                                                 "1 KB of q, 2 KB of fp32 output, 4 B of lse"}}
+
+
 def bench_translate(args, run):
     """Time indexer_translate on selections shaped like the step's top-k output
     (k sorted distinct visible positions per row, -1 padding on short rows), and the
@@ -621,10 +670,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time, headline")
     ap.add_argument("--cpu-budget-per-config", type=float, default=6.0)
-    ap.add_argument("--op", default="step", choices=["step", "q_prep", "translate"],
+    ap.add_argument("--op", default="step", choices=["step", "q_prep", "translate", "attention"],
                     help="step: the indexer step (default); q_prep: the query preparation alone, on "
                          "the workload's queries; translate: logical -> physical translation of "
-                         "top-k-shaped selections, and what the fused slots add to score + top-k")
+                         "top-k-shaped selections, and what the fused slots add to score + top-k; "
+                         "attention: sparse attention over 32 rows x top-512 slots")
+    ap.add_argument("--heads", type=int, default=16, help="query heads of --op attention")
+    ap.add_argument("--no-attention", action="store_true", help="skip the sparse-attention block")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -655,6 +707,15 @@ def main():
         run = Runner(args.workload, args.replicas)
         fn = bench_q_prep if args.op == "q_prep" else bench_translate
         print(json.dumps(fn(args, run)), flush=True)
+        return
+    if args.op == "attention":
+        res = bench_attention(probes, args.steps, args.warmup, args.heads)
+        print(json.dumps({"metric": "sparse-attention rows/s over top-k selected KV slots at 1 GPU",
+                          "value": res["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": res["ms_per_launch"], "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": res["workload"], "parallelism": "single GPU"}, **res}),
+              flush=True)
         return
 
     peaks = None if args.no_peaks else probes.peaks()
@@ -702,6 +763,9 @@ def main():
             wl.key_dtype = kd
             per[name] = measure(name, args, probes, peaks, wl=wl, cpu_budget=args.cpu_budget_per_config)
         line["per_config"] = per
+    if not args.no_attention:    # the consumer of the selections, at the decode-batch shape
+        line["sparse_attention"] = {f"heads_{h}": bench_attention(probes, max(args.steps, 20), args.warmup, h)
+                                    for h in (16, 64)}
     print(json.dumps(line), flush=True)
 
 
