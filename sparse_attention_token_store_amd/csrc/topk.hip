@@ -7,10 +7,11 @@
 // chunk of up to 36,864 elements held in registers.  Thread t holds, for each
 // group g < R/4, the four consecutive elements g*4096 + 4t .. +3 (one 16-byte load),
 // so every position-ordered scan runs once per group of four, on packed counts.
-//  1. Lower bound.  With k <= 1024 the threads are split into >= k groups; every
-//     group owns a key >= its group maximum, so the smallest group maximum t_lo has
-//     at least k keys at or above it and the k-th largest key tau >= t_lo.  Keys
-//     below t_lo (typically 80-90% of a row) take no further part.
+//  1. Lower bound.  Every thread's largest and second largest key are distinct
+//     elements of the chunk, so any value t_lo with at least k of these 2048 values
+//     at or above it has tau >= t_lo, tau being the k-th largest key.  t_lo is the
+//     lower edge of the histogram bin holding the k-th largest of them (k <= 2048).
+//     Keys below t_lo (typically 95-97% of a row) take no further part.
 //  2. The live keys (>= t_lo) are compacted, in position order, into an LDS list
 //     with their positions.  (If they do not fit, e.g. long runs of equal scores,
 //     the same steps run over the registers instead.)
@@ -97,48 +98,44 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 
 // Run by one wavefront: find the bin (of nbins = 64 * PER, or fewer when PER = 1)
 // that holds the rem-th largest counted key, scanning from the top bin down.
-// Lane l owns the PER contiguous bins [nbins - (l+1)*PER, nbins - l*PER), read with
-// independent vector loads.  Writes info = {bin, count above the bin, count in it}.
+// Lane l owns the PER contiguous bins [nbins - (l+1)*PER, nbins - l*PER).  First
+// every lane sums its bins (reading its 16-byte pieces in a lane-rotated order, so
+// that lanes PER words apart do not all hit one LDS bank) and a prefix sum over the
+// lanes finds the lane whose bins hold the rem-th key; then PER lanes take one bin
+// each of that lane's range, top bin first, and a second prefix sum finds the bin.
+// Writes info = {bin, count above the bin, count in it}; nothing when fewer than
+// rem keys were counted.
 template <int PER>
 __device__ __forceinline__ void find_bin_t(const int* hist, int nbins, int rem, int* info) {
   const int lane = lane_id();
   const int lo = nbins - (lane + 1) * PER;
-  const bool has = lo >= 0;
-  int h[PER];
-  if constexpr (PER >= 4) {
-#pragma unroll
-    for (int q = 0; q < PER / 4; ++q) {
-      const int4 v = has ? reinterpret_cast<const int4*>(hist + lo)[q] : make_int4(0, 0, 0, 0);
-      h[4 * q] = v.x;
-      h[4 * q + 1] = v.y;
-      h[4 * q + 2] = v.z;
-      h[4 * q + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < PER; ++q) h[q] = has ? hist[lo + q] : 0;
-  }
   int cnt = 0;
+  if (lo >= 0) {
+    if constexpr (PER >= 4) {
 #pragma unroll
-  for (int q = 0; q < PER; ++q) cnt += h[q];
-  const int x = (int)wave_incl_scan((uint32_t)cnt);
-  const int excl = x - cnt;
-  if (has && excl < rem && x >= rem) {
-    int above = excl, bin = -1, hb = 0;
-#pragma unroll
-    for (int q = PER - 1; q >= 0; --q) {  // from this lane's top bin down
-      if (bin < 0) {
-        if (above + h[q] >= rem) {
-          bin = lo + q;
-          hb = h[q];
-        } else {
-          above += h[q];
-        }
+      for (int q = 0; q < PER / 4; ++q) {
+        const int qq = (q + lane) & (PER / 4 - 1);
+        const int4 v = reinterpret_cast<const int4*>(hist + lo)[qq];
+        cnt += v.x + v.y + v.z + v.w;
       }
+    } else {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) cnt += hist[lo + q];
     }
-    info[0] = bin;
-    info[1] = above;
-    info[2] = hb;
+  }
+  const int x = (int)wave_incl_scan((uint32_t)cnt);  // this lane's bins and all above
+  const uint64_t hit = __ballot(x >= rem);           // (x does not decrease with the lane)
+  if (hit == 0) return;
+  const int L = __builtin_ctzll(hit);
+  const int above = __builtin_amdgcn_readlane(x - cnt, L);
+  const int top = nbins - L * PER - 1;  // lane L's top bin
+  const int h = lane < PER ? hist[top - lane] : 0;
+  const int y = (int)wave_incl_scan((uint32_t)h) + above;
+  const int J = __builtin_ctzll(__ballot(lane < PER && y >= rem));
+  if (lane == J) {
+    info[0] = top - J;
+    info[1] = y - h;
+    info[2] = h;
   }
 }
 
@@ -188,13 +185,13 @@ __device__ __forceinline__ int64_t physical_slot(const SlotMap& m, int64_t r, in
 }
 
 // kFirst: source is the score matrix; else a candidate list.  kLast: write the
-// final out_idx / out_scores (and the slots of map); else the next candidate list.  vec: 16-byte loads of
+// final out_idx / out_scores (and the slots of map); else the next candidate list.  kVec: 16-byte loads of
 // the source are aligned (score rows with ld % 4 == 0; lists always).
-template <int R, bool kFirst, bool kLast>
+template <int R, bool kFirst, bool kLast, bool kVec>
 __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     const float* __restrict__ scores, int64_t ld, Lists src, Lists dst,
     const int32_t* __restrict__ row_len, int max_row_len, int k, int nlevel, LevelChunks chunks,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_scores, SlotMap map, int vec) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_scores, SlotMap map) {
   static_assert(R % 4 == 0, "slots come in groups of four");
   constexpr int G = R / 4;             // groups of four per thread
   constexpr int C = R * kThreads;      // chunk length
@@ -235,34 +232,36 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   // Slots past the chunk's end hold the sentinel key 0; real keys are clamped to
   // >= 2^21 (this only touches negative-NaN bit patterns) and the lower bound is
   // never below 2^21, so the sentinel is never counted or selected.
+  // Every load is issued before the first is consumed: the loads take no branch
+  // (a group past the chunk's end reads the chunk's first elements instead, and
+  // its values are then masked), so their latencies overlap.
   uint32_t key[R];
+  {
+    uint32_t raw[R];
+    if constexpr (!kFirst || kVec) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int l0 = li_of(g, 0);
-    uint32_t kv[4] = {0u, 0u, 0u, 0u};
-    if (l0 < nc) {
-      if constexpr (kFirst) {
-        const float* p = scores + (int64_t)r * ld + base + l0;
-        if (vec) {
-          const float4 v = *reinterpret_cast<const float4*>(p);
-          kv[0] = order_key(v.x);
-          kv[1] = order_key(v.y);
-          kv[2] = order_key(v.z);
-          kv[3] = order_key(v.w);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kv[e] = l0 + e < nc ? order_key(p[e]) : 0u;
-        }
-      } else {
-        const uint4 v = *reinterpret_cast<const uint4*>(src.keys + (int64_t)r * src.cap + base + l0);
-        kv[0] = v.x;
-        kv[1] = v.y;
-        kv[2] = v.z;
-        kv[3] = v.w;
+      for (int g = 0; g < G; ++g) {
+        const int l0 = li_of(g, 0), at = l0 < nc ? l0 : 0;
+        uint4 v;
+        if constexpr (kFirst)
+          v = *reinterpret_cast<const uint4*>(scores + (int64_t)r * ld + base + at);
+        else
+          v = *reinterpret_cast<const uint4*>(src.keys + (int64_t)r * src.cap + base + at);
+        raw[4 * g] = v.x;
+        raw[4 * g + 1] = v.y;
+        raw[4 * g + 2] = v.z;
+        raw[4 * g + 3] = v.w;
       }
+    } else {  // rows not 16-byte aligned: element loads, clamped into the chunk
+      const float* p = scores + (int64_t)r * ld + base;
+#pragma unroll
+      for (int j = 0; j < R; ++j) raw[j] = __float_as_uint(p[min(li_of(j >> 2, j & 3), nc - 1)]);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) key[4 * g + e] = l0 + e < nc ? max(kv[e], kMinKey) : 0u;
+    for (int j = 0; j < R; ++j) {
+      const uint32_t kv = kFirst ? order_key(__uint_as_float(raw[j])) : raw[j];
+      key[j] = li_of(j >> 2, j & 3) < nc ? max(kv, kMinKey) : 0u;
+    }
   }
 
   auto emit = [&](int pos, int li, uint32_t kv) {
@@ -307,32 +306,53 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     return;
   }
 
-  // ---- 1. row maximum and the group-maximum lower bound t_lo
-  uint32_t tmax = 0u;
+  // ---- 1. row maximum and the lower bound t_lo: the k-th largest of the 2048
+  // values formed by every thread's largest and second largest key (each a distinct
+  // element of the chunk, so at least k keys lie at or above it), located to an
+  // 11-bit histogram bin and rounded down to that bin's lower edge
+  for (int b = tid; b < 2048; b += kThreads) hist[b] = 0;
+  uint32_t m1 = 0u, m2 = 0u;
 #pragma unroll
-  for (int j = 0; j < R; ++j) tmax = max(tmax, key[j]);
-  uint32_t gmax = tmax;
-  if (k <= kThreads) {
-    int gl = 1;  // lanes per group: the largest power of two <= 64 leaving >= k groups
-    while (gl < 64 && kThreads / (2 * gl) >= k) gl *= 2;
-    for (int m = 1; m < gl; m <<= 1) gmax = max(gmax, (uint32_t)__shfl_xor((int)gmax, m));
+  for (int j = 0; j < R; ++j) {
+    m2 = max(m2, min(m1, key[j]));
+    m1 = max(m1, key[j]);
   }
   {
-    const uint32_t wmax = wave_max_u32(tmax), wmin = wave_min_u32(gmax);
+    // the smallest maximum over threads that hold a key (m1 = 0: none)
+    const uint32_t wmax = wave_max_u32(m1), wmin = wave_min_u32(m1 ? m1 : 0xFFFFFFFFu);
     if (lane == 0) {
       red_max[wave] = wmax;
       red_min[wave] = wmin;
     }
-    if (tid == 0) ncand = 0;
+    if (tid == 0) {
+      ncand = 0;
+      info[0] = -1;
+    }
   }
   __syncthreads();
-  uint32_t M = 0u, tlo = 0xFFFFFFFFu;
+  uint32_t M = 0u, lo = 0xFFFFFFFFu;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     M = max(M, red_max[w]);
-    tlo = min(tlo, red_min[w]);
+    lo = min(lo, red_min[w]);
   }
-  if (k > kThreads) tlo = kMinKey;
+  uint32_t tlo = kMinKey;
+  if (k <= 2 * kThreads && lo < M) {  // (uniform)
+    // every counted value lies in [lo, M], so the bits above the highest bit in
+    // which lo and M differ are common to all of them
+    const int hi = 31 - __clz(lo ^ M);
+    const int s = hi >= 10 ? hi - 10 : 0;
+    const uint32_t dm = (1u << (hi - s + 1)) - 1u;
+    if (m1 >= lo) atomicAdd(&hist[(m1 >> s) & dm], 1);
+    if (m2 >= lo) atomicAdd(&hist[(m2 >> s) & dm], 1);
+    __syncthreads();
+    if (wave == 0) find_bin(hist, (int)dm + 1, k, info);
+    __syncthreads();
+    if (info[0] >= 0) {  // else fewer than k values were counted: no bound
+      const uint32_t pm = hi >= 31 ? 0u : (0xFFFFFFFFu << (hi + 1));
+      tlo = (M & pm) | ((uint32_t)info[0] << s);
+    }
+  }
   tlo = max(tlo, kMinKey);
 
   // ---- 2. position-ordered count of the live keys; list them in LDS if they fit
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
       int at = (int)(tab[g * kWaves + wave] + lex[g]);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (key[4 * g + e] >= tlo && (unsigned)at < (unsigned)kListMax) {
+        if (key[4 * g + e] >= tlo) {  // (at < L <= kListMax)
           lkey[at] = key[4 * g + e];
           lpos[at] = li_of(g, e);
           ++at;
@@ -527,11 +547,16 @@ hipError_t launch_level(int R, dim3 grid, hipStream_t s, const float* scores, in
                         Lists src, Lists dst, const int32_t* row_len, int max_row_len, int k,
                         int nlevel, LevelChunks chunks, int32_t* out_idx, float* out_scores,
                         const SlotMap& map, int vec) {
-#define DSA_TOPK_CASE(RR)                                                                      \
-  case RR:                                                                                     \
-    hipLaunchKernelGGL((topk_level_kernel<RR, kFirst, kLast>), grid, dim3(kThreads), 0, s,    \
-                       scores, ld, src, dst, row_len, max_row_len, k, nlevel, chunks, out_idx, \
-                       out_scores, map, vec);                                                  \
+#define DSA_TOPK_CASE(RR)                                                                             \
+  case RR:                                                                                            \
+    if (vec || !kFirst)                                                                               \
+      hipLaunchKernelGGL((topk_level_kernel<RR, kFirst, kLast, true>), grid, dim3(kThreads), 0, s,    \
+                         scores, ld, src, dst, row_len, max_row_len, k, nlevel, chunks, out_idx,      \
+                         out_scores, map);                                                            \
+    else                                                                                              \
+      hipLaunchKernelGGL((topk_level_kernel<RR, kFirst, kLast, !kFirst>), grid, dim3(kThreads), 0, s, \
+                         scores, ld, src, dst, row_len, max_row_len, k, nlevel, chunks, out_idx,      \
+                         out_scores, map);                                                            \
     break;
   switch (R) {
     DSA_TOPK_CASE(4)
