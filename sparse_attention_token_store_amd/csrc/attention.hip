@@ -326,31 +326,43 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 }
 
 // Merge of a row's split results, in split order: one workgroup per (row, 4 heads),
-// thread t takes head 4*blockIdx.x + t/64 and dims 8*(t%64) .. +7.
+// thread t takes head 4*blockIdx.x + t/64 and dims 8*(t%64) .. +7.  The splits are
+// folded in one pass with a running maximum (the output and sum rescaled when it
+// moves), eight at a time with all eight splits' loads issued before the first is
+// used.
 __global__ __launch_bounds__(256) void attn_merge_kernel(int heads, int nsplit, const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, float* __restrict__ out,
                                                          float* __restrict__ lse) {
+  constexpr int kBatch = 8;
   const int t = threadIdx.x, r = blockIdx.y;
   const int h = 4 * blockIdx.x + (t >> 6), d0 = 8 * (t & 63);
-  float M = -INFINITY;
-  bool bad = false;
-  for (int j = 0; j < nsplit; ++j) {
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (((int64_t)r * nsplit + j) * heads + h) * 2);
-    M = fmaxf(M, ml.x);
-    bad = bad || (ml.y != ml.y);
-  }
-  float z = 0.0f;
+  float M = -INFINITY, z = 0.0f;
   float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
-  if (M != -INFINITY) {
-    for (int j = 0; j < nsplit; ++j) {
-      const int64_t base = ((int64_t)r * nsplit + j) * heads + h;
-      const float2 ml = *reinterpret_cast<const float2*>(part_ml + base * 2);
-      const float w = exp2f(ml.x - M);  // 0 for a split that saw nothing
+  bool bad = false;
+  for (int j0 = 0; j0 < nsplit; j0 += kBatch) {
+    float2 ml[kBatch];
+    float4 a[kBatch], b[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {  // (past the last split: the last split again, unused)
+      const int64_t base = ((int64_t)r * nsplit + min(j0 + i, nsplit - 1)) * heads + h;
+      ml[i] = *reinterpret_cast<const float2*>(part_ml + base * 2);
       const float4* po = reinterpret_cast<const float4*>(part_o + base * kKvDim + d0);
-      const float4 a = po[0], b = po[1];
-      z += w * ml.y;
-      o0.x += w * a.x; o0.y += w * a.y; o0.z += w * a.z; o0.w += w * a.w;
-      o1.x += w * b.x; o1.y += w * b.y; o1.z += w * b.z; o1.w += w * b.w;
+      a[i] = po[0];
+      b[i] = po[1];
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (j0 + i >= nsplit) break;
+      bad = bad || (ml[i].y != ml[i].y);
+      if (ml[i].x == -INFINITY) continue;  // a split that saw nothing
+      const float Mn = fmaxf(M, ml[i].x);
+      const float c0 = exp2f(M - Mn), c1 = exp2f(ml[i].x - Mn);  // (M = -inf: c0 = 0)
+      z = z * c0 + ml[i].y * c1;
+      o0.x = o0.x * c0 + a[i].x * c1; o0.y = o0.y * c0 + a[i].y * c1;
+      o0.z = o0.z * c0 + a[i].z * c1; o0.w = o0.w * c0 + a[i].w * c1;
+      o1.x = o1.x * c0 + b[i].x * c1; o1.y = o1.y * c0 + b[i].y * c1;
+      o1.z = o1.z * c0 + b[i].z * c1; o1.w = o1.w * c0 + b[i].w * c1;
+      M = Mn;
     }
   }
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;
