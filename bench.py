@@ -77,7 +77,8 @@ def source_hash(files):
 KERNEL_SOURCES = {"score_decode": ["score_decode.hip", "common.hpp"],
                   "score_prefill": ["score_prefill.hip", "common.hpp"],
                   "q_prep": ["store.hip", "common.hpp"],
-                  "translate": ["topk.hip", "common.hpp"]}
+                  "translate": ["topk.hip", "common.hpp"],
+                  "sparse_attention": ["attention.hip", "common.hpp"]}
 
 
 def traffic_from_profile(kernel: str, workload: str):
@@ -400,12 +401,15 @@ def bench_attention(probes, steps, warmup, heads, rows=32, k=512, num_slots=4239
     splits_ws = dsa.attention_workspace_bytes(rows, k, heads)
     del kv, sl
     torch.cuda.empty_cache()
+    traffic = traffic_from_profile("sparse_attention", f"decode_b32_h{heads}") \
+        if (rows, k, num_slots) == (32, 512, 423936) else None
     return {"workload": f"sparse attention, {rows} rows x top-{k} slots, {heads} heads x 512, bf16 KV",
             "ms_per_launch": ms, "rows_per_s": rows / (ms / 1e3),
             "kv_rows_per_s": rows * k / (ms / 1e3), "heads": heads, "rows": rows, "k": k,
             "split_workspace_bytes": splits_ws,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "algorithmic_per_launch": nbytes,
+                         "traffic": traffic,
                          "algorithmic_per_unit": "1024 B per listed KV row + 8 B slot; per row and head "
                                                  "1 KB of q, 2 KB of fp32 output, 4 B of lse"}}
 
