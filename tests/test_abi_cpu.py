@@ -172,14 +172,34 @@ def test_topk_plan_at_the_largest_sizes():
     # half of each first-level chunk); the host-side plan must size them without
     # overrunning its tables, and the workspace must cover two candidate lists of
     # the first level's survivors
+    # The plan: first-level chunks of 16,384 (doubled until >= 2k), or twice that where
+    # it saves a whole level; later levels of 8k (a power of two, at most 32,768) until
+    # one 36,864-element chunk is left.
+    def after(m, c, k):
+        return (m // c) * min(k, c) + min(m % c, k)
+
+    def levels(n, k, first):
+        c0 = first
+        while c0 < 2 * k:
+            c0 *= 2
+        m, lv, c = n, 0, c0
+        while m > 36864:
+            m = after(m, c, k)
+            lv += 1
+            c = 4096
+            while c < 8 * k and c < 32768:
+                c *= 2
+        return lv + 1, c0
+
     lib = dsa.load_library()
     for rows, n, k in [(1, 2**31 - 1, 8192), (1, 2**31 - 1, 1), (3, 2**31 - 1, 4097),
-                       (65535, 2**31 - 1, 8192), (1, 36865, 8192), (1, 1 << 20, 8192)]:
+                       (65535, 2**31 - 1, 8192), (1, 36865, 8192), (1, 1 << 20, 8192),
+                       (4, 1 << 20, 1024), (16, 131072, 1024)]:
         need = lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, rows, n, k)
-        chunk0 = 16384
-        while chunk0 < 2 * k:
-            chunk0 *= 2
-        survivors = (n // chunk0) * min(k, chunk0) + min(n % chunk0, k)
+        la, ca = levels(n, k, 16384)
+        lb, cb = levels(n, k, 32768)
+        chunk0 = cb if la > 2 and lb < la else ca
+        survivors = after(n, chunk0, k)
         assert need >= 2 * rows * survivors * 8, (rows, n, k, need)
         assert need == lib.indexer_workspace_bytes(dsa.IDX_OP_TOPK, rows, n, k)   # deterministic
         both = lib.indexer_workspace_bytes(dsa.IDX_OP_SCORE_TOPK, rows, n, k)
