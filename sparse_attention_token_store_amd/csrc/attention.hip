@@ -8,8 +8,12 @@
 //
 // Design for gfx950:
 //  - A workgroup of four wavefronts takes one row, one run of its slot list (a
-//    split) and up to 64 heads: 16 heads per wavefront, and with fewer than 64 heads
-//    the wavefronts of a head group split its 512 output dims.  The run is streamed
+//    split) and 16 or 32 heads: the wavefronts of a 16-head group split its 512
+//    output dims 4 or 2 ways.  With more than 32 heads, further workgroups take the
+//    further 32-head groups; each reads the run's KV rows again (mostly from L2),
+//    whereas a 64-head workgroup held all 512 output dims of its 16 heads in each
+//    wavefront's registers, one wavefront per SIMD, and was slower (27.2 against
+//    24.2 us for 32 rows x top-512 with 64 heads).  The run is streamed
 //    in stages of 32 KV rows (32 KB of bf16) that LDS DMA (global_load_lds, one 1 KB
 //    row per wavefront instruction, non-temporal: every row is read once) copies into
 //    a ring of three LDS stages, two in flight while the third is scored.
@@ -388,7 +392,7 @@ struct SplitPlan {
 // split longer than its LDS slot table.
 SplitPlan plan_splits(int rows, int k, int heads) {
   if (k <= 0) return SplitPlan{1, kStageKeys};
-  const int hgroups = (heads + 63) / 64;
+  const int hgroups = (heads + 31) / 32;
   const int stages = (k + kStageKeys - 1) / kStageKeys;
   int s = (256 + rows * hgroups - 1) / (rows * hgroups);
   s = std::min(s, std::max(1, stages / 2));
@@ -414,7 +418,7 @@ hipError_t launch_attention(const uint16_t* q, int heads, const uint8_t* kv, int
   const SplitPlan p = plan_splits(rows, k, heads);
   float* part_o = static_cast<float*>(ws);
   float* part_ml = p.splits > 1 ? part_o + (size_t)rows * p.splits * heads * kKvDim : nullptr;
-  const int wg_heads = heads < 64 ? heads : 64;
+  const int wg_heads = heads < 32 ? heads : 32;
   const dim3 grid((unsigned)p.splits, (unsigned)rows, (unsigned)(heads / wg_heads));
   const float scale_log2 = scale * kLog2e;
   switch (64 / wg_heads) {  // dim parts per head group
@@ -423,8 +427,7 @@ hipError_t launch_attention(const uint16_t* q, int heads, const uint8_t* kv, int
     hipLaunchKernelGGL((attn_split_kernel<DP, RING>), grid, dim3(256), 0, s, q, heads, kv, num_slots, slots, \
                        ld, k, scale_log2, p.keys_per_split, out, lse, part_o, part_ml);                     \
     break;
-    DSA_ATTN_CASE(1, 3)   // 104 KB of LDS: one workgroup per CU, two stages in flight
-    DSA_ATTN_CASE(2, 3)
+    DSA_ATTN_CASE(2, 3)   // 104 KB of LDS: one workgroup per CU, two stages in flight
     DSA_ATTN_CASE(4, 2)   // 72 KB: two workgroups per CU, one stage in flight each
 #undef DSA_ATTN_CASE
     default:
