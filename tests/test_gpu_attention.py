@@ -76,6 +76,8 @@ CASES = [
     (2, 16, 3000, 40000, 0.05, 2.0),       # several splits per row
     (2, 128, 2048, 40000, 0.0, 1.0),
     (1, 64, 5000, 8000, 0.3, 1.0),         # split lists longer than one slot table
+    (1, 16, 65536, 70000, 0.1, 1.0),       # the longest list the entry point accepts
+    (3, 128, 777, 20000, 0.0, 2.0),        # four 32-head workgroups per row
 ]
 
 

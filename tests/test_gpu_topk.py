@@ -42,6 +42,8 @@ CASES = [
     (2, 131072, 1024, "normal"),
     (2, 131072, 1024, "ties"),
     (1, 200000, 2048, "heavy"),
+    # 32,768-element first-level chunks (they save a level here), a partial last chunk
+    (2, 600000, 1024, "ties"),
     (2, 100000, 8192, "normal"),
     # k <= 512 on long rows: the later levels use 4096-element chunks (R = 4)
     (2, 131072, 512, "heavy"),
