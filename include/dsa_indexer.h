@@ -301,17 +301,24 @@ int32_t indexer_translate(const int32_t* idx, int64_t ld_idx, int32_t k, idx_kca
  * A row that lists nothing gets out = 0 and lse = -inf; a listed slot >= num_slots
  * is never read and makes its row's out and lse NaN.  Scores and sums are fp32;
  * the probabilities meet the KV states in bf16 (MFMA) with fp32 accumulation.
- *   q          device bf16 [rows][heads][512].
+ *   q          device bf16 [rows][heads][512], 16-byte aligned.
  *   heads      16, 32, 64 or 128 query heads.
  *   kv         device bf16 [num_slots][512]: slot s = block*block_size + offset of
- *              a paged cache with 512*2-byte tokens (any block size), 16-byte aligned.
- *   slots      device int64 [rows][ld_slots]: the first k entries of each row are
- *              its list (indexer_score_topk's out_slots or indexer_translate's).
- *   k          0 .. 65536.  scale  finite, > 0 (e.g. 1/sqrt(512)).
+ *              a paged cache with 512*2-byte tokens (any block size), 16-byte
+ *              aligned; num_slots 1 .. INT32_MAX.
+ *   slots      device int64 [rows][ld_slots], 8-byte aligned, ld_slots >= k: the
+ *              first k entries of each row are its list (indexer_score_topk's
+ *              out_slots or indexer_translate's); may be NULL when k = 0.
+ *   k          0 .. 65536.  rows  0 .. 65535.  scale  finite, > 0 (e.g. 1/sqrt(512)).
  *   out        device fp32 [rows][heads][512], 16-byte aligned.
  *   lse        NULL or device fp32 [rows][heads].
  *   ws         indexer_attention_workspace_bytes(rows, k, heads) bytes (0: may be
- *              NULL), 256-byte aligned: per-split partial results.
+ *              NULL), 256-byte aligned: per-split partial results, caller-owned,
+ *              contents on entry unused.
+ * Errors: IDX_EUNSUPPORTED for another head count; IDX_EINVAL for a size, stride,
+ * scale, null or misaligned pointer out of the ranges above; IDX_EWORKSPACE for a
+ * missing or short workspace.  The caller keeps ownership of every buffer; nothing
+ * is allocated, synchronised or freed.
  */
 int32_t indexer_sparse_attention(const void* q, int32_t heads, const void* kv, int64_t num_slots,
                                  const int64_t* slots, int64_t ld_slots, int32_t k, int32_t rows,

@@ -391,7 +391,7 @@ struct SplitPlan {
 // latency-bound, so spreading a row over more CUs pays for that traffic), and no
 // split longer than its LDS slot table.
 SplitPlan plan_splits(int rows, int k, int heads) {
-  if (k <= 0) return SplitPlan{1, kStageKeys};
+  if (k <= 0 || rows <= 0) return SplitPlan{1, kStageKeys};  // nothing to split
   const int hgroups = (heads + 31) / 32;
   const int stages = (k + kStageKeys - 1) / kStageKeys;
   int s = (256 + rows * hgroups - 1) / (rows * hgroups);

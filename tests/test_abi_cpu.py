@@ -249,6 +249,54 @@ def test_translate_validation():
     assert call(rows=rows(n=0), idx=None, slots=None) == dsa.IDX_OK
 
 
+def test_sparse_attention_validation_and_workspace():
+    lib = dsa.load_library()
+    f = lib.indexer_sparse_attention
+    ws_of = lib.indexer_attention_workspace_bytes
+    need = ws_of(32, 512, 16)
+    assert need > 0 and ws_of(32, 512, 16) == dsa.attention_workspace_bytes(32, 512, 16)
+    # (the partial outputs and (max, log-sum) pairs of every split are fp32)
+    assert need % (32 * 16 * (dsa.KV_DIM + 2) * 4) == 0
+    for bad in [(-1, 512, 16), (65536, 512, 16), (32, -1, 16), (32, (1 << 16) + 1, 16), (32, 512, 24)]:
+        assert ws_of(*bad) == 0, bad
+    assert ws_of(0, 512, 16) == 0
+
+    ok = dict(q=FAKE, heads=16, kv=ALIGNED, num_slots=1000, slots=FAKE, ld_slots=512, k=512, rows=32,
+              scale=0.04, out=ALIGNED, lse=None, ws=None, ws_bytes=0)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["q"], a["heads"], a["kv"], a["num_slots"], a["slots"], a["ld_slots"], a["k"], a["rows"],
+                 a["scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+    # every call below fails validation, so nothing is launched
+    assert call(heads=24) == dsa.IDX_EUNSUPPORTED and "heads" in err(lib)
+    assert call(rows=-1) == dsa.IDX_EINVAL
+    assert call(rows=65536) == dsa.IDX_EINVAL
+    assert call(k=-1) == dsa.IDX_EINVAL
+    assert call(k=(1 << 16) + 1, ld_slots=1 << 17) == dsa.IDX_EINVAL
+    assert call(ld_slots=511) == dsa.IDX_EINVAL and "ld_slots" in err(lib)
+    assert call(num_slots=0) == dsa.IDX_EINVAL
+    assert call(num_slots=1 << 31) == dsa.IDX_EINVAL
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(scale=s) == dsa.IDX_EINVAL and "scale" in err(lib)
+    assert call(q=None) == dsa.IDX_EINVAL
+    assert call(kv=None) == dsa.IDX_EINVAL
+    assert call(out=None) == dsa.IDX_EINVAL
+    assert call(slots=None) == dsa.IDX_EINVAL
+    assert call(q=FAKE + 8) == dsa.IDX_EINVAL and "aligned" in err(lib)
+    assert call(kv=ALIGNED + 4) == dsa.IDX_EINVAL
+    assert call(out=ALIGNED + 8) == dsa.IDX_EINVAL
+    assert call(slots=FAKE + 4) == dsa.IDX_EINVAL and "slots" in err(lib)
+    assert call(lse=FAKE + 2) == dsa.IDX_EINVAL and "lse" in err(lib)
+    # a call that needs partials: no workspace, a short one, a misaligned one
+    assert call() == dsa.IDX_EWORKSPACE
+    assert call(ws=ALIGNED, ws_bytes=need - 1) == dsa.IDX_EWORKSPACE
+    assert call(ws=ALIGNED + 64, ws_bytes=need) == dsa.IDX_EINVAL and "256" in err(lib)
+    # nothing to do: no launch, no pointer needed
+    assert call(rows=0, q=None, kv=None, slots=None, out=None) == dsa.IDX_OK
+
+
 def test_static_scratch_entry_point_validation():
     # the allocation-free variant runs the same argument checks as indexer_score_topk
     # and refuses, before touching the GPU, any call whose workspace would not fit the
