@@ -169,9 +169,10 @@ int32_t index_k_store(const void* x_bf16, int64_t n, const int32_t* positions,
  *   out_bf16      NULL or device bf16 [n_vec][128].
  *   codes, scales both NULL, or device uint8 [n_vec][128] and fp32 [n_vec].
  *   prequant_dbg  NULL or device fp32 [n_vec][128]: y before rounding/quantisation.
- * At least one output must be requested.  Errors: IDX_EINVAL for a bad size, flag,
- * rope parameter, missing pointer or misaligned pointer (q_bf16, out_bf16 and
- * prequant_dbg 16-byte; codes 8-byte; scales and positions 4-byte).
+ * At least one output must be requested when n_vec > 0 (n_vec = 0 is a no-op, with
+ * any pointers).  Errors: IDX_EINVAL for a bad size, flag, rope parameter, missing
+ * pointer or misaligned pointer (q_bf16, out_bf16 and prequant_dbg 16-byte; codes
+ * 8-byte; scales and positions 4-byte).
  */
 int32_t indexer_q_prep(const void* q_bf16, int64_t n_vec, int32_t heads, const int32_t* positions,
                        uint32_t flags, float rms_eps, float rope_base, int32_t rope_dim, void* out_bf16,

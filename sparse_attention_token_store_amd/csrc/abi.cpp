@@ -201,9 +201,9 @@ IDX_API int32_t indexer_q_prep(const void* q_bf16, int64_t n_vec, int32_t heads,
   }
   if ((flags & IDX_STORE_RMSNORM) && (!(rms_eps >= 0.0f) || !std::isfinite(rms_eps)))
     return fail(IDX_EINVAL, "rms_eps must be finite and >= 0");
+  if (n_vec == 0) return IDX_OK;  // nothing to do: outputs of no elements may be NULL
   if ((codes == nullptr) != (scales == nullptr)) return fail(IDX_EINVAL, "codes and scales go together");
   if (!out_bf16 && !codes && !prequant_dbg) return fail(IDX_EINVAL, "no output requested");
-  if (n_vec == 0) return IDX_OK;
   if (n_vec > ((int64_t)1 << 40)) return fail(IDX_EINVAL, "n_vec too large");
   if ((n_vec / heads) * (((int64_t)heads + 3) / 4) > (int64_t)INT32_MAX * 4)
     return fail(IDX_EINVAL, "too many vectors for one launch (rows * ceil(heads / 4) > 4 * INT32_MAX)");

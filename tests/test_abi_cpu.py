@@ -104,6 +104,7 @@ def test_q_prep_validation():
     assert call(dbg=FAKE + 8) == dsa.IDX_EINVAL and "prequant_dbg" in err(lib)
     # no RoPE: positions may be NULL; n = 0 is a no-op that never touches the GPU
     assert call(n=0, q=None, pos=None, flags=H) == dsa.IDX_OK
+    assert call(n=0, q=None, pos=None, out=None, flags=H) == dsa.IDX_OK   # (empty outputs: NULL)
     assert err(lib) == ""
 
 
