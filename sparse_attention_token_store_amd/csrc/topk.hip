@@ -542,6 +542,22 @@ __global__ __launch_bounds__(256) void translate_kernel(const int32_t* __restric
   }
 }
 
+// The same with four consecutive entries per thread (one 16-byte index load, two
+// 16-byte slot stores, four independent table gathers), for k and both strides
+// multiples of four and 16-byte aligned lists.
+__global__ __launch_bounds__(256) void translate4_kernel(const int32_t* __restrict__ idx, int64_t ld_idx,
+                                                         int64_t rows, int k, SlotMap map) {
+  const int q = k / 4;
+  const int64_t total = rows * q;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / q, j = 4 * (e - r * q);
+    const int4 v = *reinterpret_cast<const int4*>(idx + r * ld_idx + j);
+    longlong2* o = reinterpret_cast<longlong2*>(map.slots + r * map.ld + j);
+    o[0] = make_longlong2(physical_slot(map, r, v.x), physical_slot(map, r, v.y));
+    o[1] = make_longlong2(physical_slot(map, r, v.z), physical_slot(map, r, v.w));
+  }
+}
+
 template <bool kFirst, bool kLast>
 hipError_t launch_level(int R, dim3 grid, hipStream_t s, const float* scores, int64_t ld,
                         Lists src, Lists dst, const int32_t* row_len, int max_row_len, int k,
@@ -687,6 +703,14 @@ hipError_t launch_translate(const int32_t* idx, int64_t ld_idx, int rows, int k,
                             hipStream_t s) {
   const int64_t total = (int64_t)rows * k;
   if (total == 0) return hipSuccess;
+  const bool quad = k % 4 == 0 && ld_idx % 4 == 0 && map.ld % 2 == 0 &&
+                    (reinterpret_cast<uintptr_t>(idx) & 15) == 0 && (reinterpret_cast<uintptr_t>(map.slots) & 15) == 0;
+  if (quad) {
+    const int64_t blocks = std::min<int64_t>((total / 4 + 255) / 256, 1 << 16);
+    hipLaunchKernelGGL(translate4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, idx, ld_idx, (int64_t)rows, k,
+                       map);
+    return hipGetLastError();
+  }
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 1 << 16);
   hipLaunchKernelGGL(translate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, idx, ld_idx, (int64_t)rows, k,
                      map);

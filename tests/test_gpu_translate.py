@@ -30,7 +30,7 @@ def run_translate(idx_np, table_np, row_seq_np, row_len_np, wl, max_row_len=None
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("k", [1, 333, 2048])
+@pytest.mark.parametrize("k", [1, 12, 333, 2048])  # (k % 4 == 0: four entries per thread)
 def test_translate_arbitrary_indices(k):
     wl = gen.config(2, scale=0.05)
     rng = np.random.default_rng(k)
