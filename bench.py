@@ -16,7 +16,9 @@ from HBM, not from the 256 MB last-level cache.
 Timing: the K timed steps are queued behind a device-side delay, so the GPU runs
 them back to back whatever the host's launch rate; HIP events on the launch stream
 bracket the region and every kernel in it.  A second, host-paced pass (no delay)
-is reported beside it.
+is reported beside it.  The pass with events around every kernel also gives the
+p10 / median / p90 of the step and of each kernel (`kernel_ms.p10_p50_p90`).  The
+default is 100 timed steps after 10 warm-up steps.
 
 Default run: the headline line is the chunked prefill (4096 query rows on a
 32,768-token prefix, 142.6M visible (query, key) pairs per step, the largest
@@ -599,6 +601,14 @@ def time_steps(run, probes, steps, warmup, queue_ahead=True, per_kernel=False):
     k = {"store_or_quant": float(np.mean([e[0].ms_to(e[1]) for e in evs])),
          "score": float(np.mean([e[1].ms_to(e[2]) for e in evs])),
          "topk": float(np.mean([e[2].ms_to(e[3]) for e in evs]))}
+    # p10 / median / p90 over the steps of this pass: each step between its own first
+    # and last event, and each kernel between the events around it
+    pct = lambda xs: [float(v) for v in np.percentile(xs, [10, 50, 90])]
+    k["p10_p50_p90"] = {"step": pct([e[0].ms_to(e[3]) for e in evs]),
+                        "store_or_quant": pct([e[0].ms_to(e[1]) for e in evs]),
+                        "score": pct([e[1].ms_to(e[2]) for e in evs]),
+                        "topk": pct([e[2].ms_to(e[3]) for e in evs]),
+                        "steps": steps}
     return ms, k
 
 
@@ -662,8 +672,8 @@ def measure(name, args, probes, peaks, wl=None, cpu_budget=None) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--per-config", default=",".join(PER_CONFIG),
                     help="comma-separated workloads measured after the headline (default: the other "
