@@ -20,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdsa_indexer.so")
 BENCH_OUT = os.path.join(PKG, "libdsa_bench.so")       # measurement kernels of bench.py
 BUILD_DIR = os.path.join(ROOT, "_build")
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_abi", "c_decode_step.c")   # plain C caller of the ABI
+C_CALLER_OUT = os.path.join(ROOT, "tests", "c_abi", "c_decode_step")
 
 SOURCES = ["abi.cpp", "store.hip", "score_decode.hip", "score_prefill.hip", "topk.hip", "attention.hip"]
 BENCH_SOURCES = ["bench_peaks.hip"]
@@ -62,17 +64,38 @@ def _link(objs: list[str], out: str) -> None:
     os.replace(tmp, out)
 
 
+def build_c_caller(out: str = C_CALLER_OUT) -> str:
+    """Compile the plain C caller of the library (tests/c_abi) with the host C
+    compiler.  It includes only include/dsa_indexer.h and the HIP runtime API, and
+    finds libdsa_indexer.so next to the package through a relative run path."""
+    cc = os.environ.get("CC") or shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("no host C compiler (gcc or cc) for the C caller of the library")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    rel = os.path.relpath(PKG, os.path.dirname(os.path.abspath(out)))
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), C_CALLER_SRC, "-o", out,
+           "-L", PKG, "-ldsa_indexer", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/" + rel, "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("C caller build failed:\n" + r.stdout + r.stderr)
+    return out
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compile every source and link the indexer library (and the benchmark's
-    measurement library); returns the indexer library's path."""
+    measurement library), then the plain C caller the tests run; returns the
+    indexer library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES + BENCH_SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra or []), srcs))
     _link(objs[:len(SOURCES)], OUT)
     _link(objs[len(SOURCES):], BENCH_OUT)
+    build_c_caller()
     if verbose:
-        print(f"built {OUT} and {BENCH_OUT}")
+        print(f"built {OUT}, {BENCH_OUT} and {C_CALLER_OUT}")
     return OUT
 
 
