@@ -699,7 +699,7 @@ def main():
                     help="also run a device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
+        print(json.dumps({"error": "the indexer path runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
     if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
         print("single-GPU benchmark: run without torch.distributed", file=sys.stderr)
