@@ -219,7 +219,9 @@ int32_t indexer_score(const void* q, int32_t q_dtype, const float* q_scale, cons
  * Row r selects, among positions p < row_len[r], the k largest scores, ties broken
  * by the lower position (+0 and -0 are equal).  out_idx[r] holds the selected
  * positions in ascending order followed by -1 padding when row_len[r] < k.
- * NaN scores give an unspecified (but in-bounds) selection.
+ * A NaN score, of either sign and any payload, ranks above every number, and NaNs
+ * tie among themselves (torch.topk's order): a key of a bad block id, which scores
+ * NaN, is selected first.
  *   scores   device fp32 [rows][ld];  row_len  device int32 [rows].
  *   k        1..8192.
  *   out_idx  device int32 [rows][k].

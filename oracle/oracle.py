@@ -426,7 +426,9 @@ def topk(scores: np.ndarray, row_len, k: int) -> np.ndarray:
     score descending, ties broken by the lower position, and the first
     min(k, row_len[r]) are kept.  READING (output form): the kept positions are
     returned in ascending order and the row is padded with -1 to length k.  Zero
-    scores of either sign compare equal (they are the same number).
+    scores of either sign compare equal (they are the same number).  READING (NaN):
+    a NaN score, of either sign and any payload, ranks above every number and all
+    NaNs tie, which is how torch.topk orders values.
 
     ([ATOM-1507] "Summary"/"How it was isolated": index_topk of 512 or 1024 kept
     per row; the selection kernel is judged by overlap with torch.topk.)
@@ -438,8 +440,12 @@ def topk(scores: np.ndarray, row_len, k: int) -> np.ndarray:
         n = int(row_len[r])
         if n <= 0:
             continue
-        s = scores[r, :n].astype(np.float64)
-        order = np.argsort(-s, kind="stable")          # stable: lower index first on ties
+        with np.errstate(invalid="ignore"):              # (signalling-NaN inputs)
+            s = scores[r, :n].astype(np.float64)
+        nan = np.isnan(s)
+        value = np.where(nan, 0.0, s)
+        # primary key: NaN first; then score descending; then the lower position
+        order = np.lexsort((np.arange(n), -value, ~nan))
         keep = np.sort(order[:min(k, n)])
         out[r, :keep.size] = keep
     return out

@@ -43,9 +43,22 @@ constexpr int kLevel0Chunk = 16384;    // first reducing level of long rows (R =
 constexpr int kLevelNChunk = 32768;    // largest chunk of the later reducing levels (R = 32)
 constexpr int kMaxR = 36;
 constexpr int kMaxSingle = kMaxR * kThreads;   // 36,864: one chunk
-constexpr uint32_t kMinKey = 1u << 21;  // smallest key a real element may take
+constexpr uint32_t kMinKey = 1u << 21;  // floor of the lower bound (below every real key)
 constexpr int kListMax = 8192;          // live keys held in the LDS list
 constexpr int kRankMax = 128;           // boundary bins this small are settled by ranking
+
+// Score -> unsigned key with the same order (larger score, larger key), in the order
+// torch.topk ranks values: -0 and +0 map to one key, and every NaN, of either sign
+// and any payload, maps to the largest key, above +inf.  The smallest key, that of
+// -inf, is 0x007FFFFF.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __builtin_isnan(f) ? 0x7FFFFFFFu : __float_as_uint(f);
+  u = (u == 0x80000000u) ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
 // number of candidates a row keeps after one level with chunk size C
 __device__ __host__ __forceinline__ int64_t after_level(int64_t n, int64_t C, int k) {
@@ -229,9 +242,9 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   // element 4*g + e of this thread sits at chunk offset li(g, e)
   auto li_of = [&](int g, int e) { return g * 4 * kThreads + 4 * tid + e; };
 
-  // Slots past the chunk's end hold the sentinel key 0; real keys are clamped to
-  // >= 2^21 (this only touches negative-NaN bit patterns) and the lower bound is
-  // never below 2^21, so the sentinel is never counted or selected.
+  // Slots past the chunk's end hold the sentinel key 0; a real key is at least
+  // 0x007FFFFF (-inf) and the lower bound is never below kMinKey = 2^21, so the
+  // sentinel is never counted or selected.
   // Every load is issued before the first is consumed: the loads take no branch
   // (a group past the chunk's end reads the chunk's first elements instead, and
   // its values are then masked), so their latencies overlap.
@@ -260,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const uint32_t kv = kFirst ? order_key(__uint_as_float(raw[j])) : raw[j];
-      key[j] = li_of(j >> 2, j & 3) < nc ? max(kv, kMinKey) : 0u;
+      key[j] = li_of(j >> 2, j & 3) < nc ? kv : 0u;
     }
   }
 

@@ -94,3 +94,26 @@ def test_topk_deterministic():
     a = run_topk(x, lens, 40000, 1024)
     b = run_topk(x, lens, 40000, 1024)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("n,k", [(3000, 512), (36000, 1024), (200000, 1024)])
+def test_topk_nan_inf_and_signed_zero_order(n, k):
+    """NaNs of both signs and several payloads rank above +inf and tie among
+    themselves (torch.topk's order), -0 equals +0, and infinities sit at the ends:
+    bit-exact against the oracle, at one reducing level and at several."""
+    rng = np.random.default_rng(n)
+    rows = 3
+    x = (rng.integers(-20, 21, size=(rows, n)).astype(np.float32) * np.float32(0.5))
+    nan_bits = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF, 0x7FFFFFFF], dtype=np.uint32)
+    for r in range(rows):
+        m = [k // 4, k + 37, 3][r]                      # fewer NaNs than k, more than k, a few
+        at = rng.choice(n, m, replace=False)
+        x[r, at] = nan_bits[rng.integers(0, 5, size=m)].view(np.float32)
+        x[r, rng.choice(n, 20, replace=False)] = np.float32(np.inf)
+        x[r, rng.choice(n, 20, replace=False)] = np.float32(-np.inf)
+        x[r, rng.choice(n, 50, replace=False)] = np.float32(-0.0)
+    lens = np.array([n, n - 17, n // 2], np.int64)
+    got = run_topk(x, lens, n, k)
+    want = O.topk(x, lens, k)
+    for r in range(rows):
+        assert np.array_equal(got[r], want[r]), (r, np.setdiff1d(got[r], want[r])[:5])

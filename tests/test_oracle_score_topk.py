@@ -162,6 +162,33 @@ def test_topk_matches_torch_topk_on_distinct_values():
         assert np.array_equal(np.sort(t), got[r, :t.size])
 
 
+def _nan_f32(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+def test_topk_nan_order_matches_torch_topk():
+    # NaNs of both signs and several payloads rank above +inf, as in torch.topk
+    nans = [_nan_f32(b) for b in (0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF)]
+    rng = np.random.default_rng(2)
+    for trial in range(20):
+        n = int(rng.integers(8, 400))
+        x = (rng.permutation(n).astype(np.float32) - n / 2) * np.float32(0.25)
+        m = int(rng.integers(1, min(n, 12)))
+        at = rng.choice(n, m, replace=False)
+        x[at] = [nans[i % 4] for i in range(m)]
+        x[rng.integers(n)] = np.float32(np.inf) if m < n else x[0]
+        for k in (m, m + 1, min(n, m + 7)):
+            got = O.topk(x[None], [n], k)[0]
+            t = torch.topk(torch.from_numpy(x), k).indices.numpy()
+            assert np.array_equal(np.sort(t), got[:k]), (trial, k)
+    # worked row: NaNs first, then +inf, then the largest numbers; NaNs tie by position
+    row = np.array([1.0, nans[1], 3.0, np.inf, nans[0], -np.inf, nans[2]], dtype=np.float32)
+    assert O.topk(row[None], [7], 4)[0].tolist() == [1, 3, 4, 6]
+    assert O.topk(row[None], [7], 2)[0].tolist() == [1, 4]
+    assert O.topk(row[None], [7], 5)[0].tolist() == [1, 2, 3, 4, 6]
+    assert O.topk(row[None], [6], 7)[0].tolist() == [0, 1, 2, 3, 4, 5, -1]
+
+
 # ---------------------------------------------------------------- jaccard --------
 
 def test_jaccard_reproduces_printed_table():
