@@ -7,10 +7,11 @@
 // chunk of up to 36,864 elements held in registers.  Thread t holds, for each
 // group g < R/4, the four consecutive elements g*4096 + 4t .. +3 (one 16-byte load),
 // so every position-ordered scan runs once per group of four, on packed counts.
-//  1. Lower bound.  Every thread's largest and second largest key are distinct
-//     elements of the chunk, so any value t_lo with at least k of these 2048 values
-//     at or above it has tau >= t_lo, tau being the k-th largest key.  t_lo is the
-//     lower edge of the histogram bin holding the k-th largest of them (k <= 2048).
+//  1. Lower bound.  Every thread splits its keys into four sets (element e of each
+//     of its groups) and takes each set's maximum: 4096 distinct elements of the
+//     chunk, so any value t_lo with at least k of them at or above it has
+//     tau >= t_lo, tau being the k-th largest key.  t_lo is the lower edge of the
+//     histogram bin holding the k-th largest of them (k <= 4096).
 //     Keys below t_lo (typically 95-97% of a row) take no further part.
 //  2. The live keys (>= t_lo) are compacted, in position order, into an LDS list
 //     with their positions.  (If they do not fit, e.g. long runs of equal scores,
@@ -48,16 +49,21 @@ constexpr int kListMax = 8192;          // live keys held in the LDS list
 constexpr int kRankMax = 128;           // boundary bins this small are settled by ranking
 
 // Score -> unsigned key with the same order (larger score, larger key), in the order
-// torch.topk ranks values: -0 and +0 map to one key, and every NaN, of either sign
-// and any payload, maps to the largest key, above +inf.  The smallest key, that of
-// -inf, is 0x007FFFFF.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __builtin_isnan(f) ? 0x7FFFFFFFu : __float_as_uint(f);
-  u = (u == 0x80000000u) ? 0u : u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// torch.topk ranks values.  A non-negative score gets the top bit set; a negative one
+// becomes its two's complement, which reverses the order of the negative scores and
+// puts -0 on the key of +0 (0x80000000).  The smallest key, that of -inf, is 0x00800000.
+// NaNs are left to nan_key: here a NaN of positive sign lands above the key of +inf
+// and one of negative sign below the key of -inf.
+__device__ __forceinline__ uint32_t order_key_raw(uint32_t u) {
+  return (int32_t)u < 0 ? 0u - u : (u | 0x80000000u);
+}
+// Every NaN, of either sign and any payload, takes the largest key, above +inf (NaNs
+// tie among themselves); other keys, and the sentinel 0, pass unchanged.
+__device__ __forceinline__ uint32_t nan_key(uint32_t key) {
+  return (key > 0xFF800000u || key - 1u < 0x007FFFFFu) ? 0xFFFFFFFFu : key;
 }
 __device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : 0u - k);
 }
 
 // number of candidates a row keeps after one level with chunk size C
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   auto li_of = [&](int g, int e) { return g * 4 * kThreads + 4 * tid + e; };
 
   // Slots past the chunk's end hold the sentinel key 0; a real key is at least
-  // 0x007FFFFF (-inf) and the lower bound is never below kMinKey = 2^21, so the
+  // 0x00800000 (-inf) and the lower bound is never below kMinKey = 2^21, so the
   // sentinel is never counted or selected.
   // Every load is issued before the first is consumed: the loads take no branch
   // (a group past the chunk's end reads the chunk's first elements instead, and
@@ -270,11 +276,27 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
 #pragma unroll
       for (int j = 0; j < R; ++j) raw[j] = __float_as_uint(p[min(li_of(j >> 2, j & 3), nc - 1)]);
     }
+    uint64_t nan_lanes = 0;  // lanes of this wave that loaded a NaN score
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const uint32_t kv = kFirst ? order_key(__uint_as_float(raw[j])) : raw[j];
-      key[j] = li_of(j >> 2, j & 3) < nc ? kv : 0u;
+      if constexpr (kFirst) {
+        nan_lanes |= __ballot(__builtin_isnan(__uint_as_float(raw[j])));
+        key[j] = order_key_raw(raw[j]);
+      } else {
+        key[j] = raw[j];
+      }
     }
+    if (nan_lanes != 0) {  // (uniform; rare)
+#pragma unroll
+      for (int j = 0; j < R; ++j) key[j] = nan_key(key[j]);
+    }
+    // only the groups that reach past the chunk's end hold slots to mask (uniform test)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if ((g + 1) * 4 * kThreads > nc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[4 * g + e] = li_of(g, e) < nc ? key[4 * g + e] : 0u;
+      }
   }
 
   auto emit = [&](int pos, int li, uint32_t kv) {
@@ -319,17 +341,18 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     return;
   }
 
-  // ---- 1. row maximum and the lower bound t_lo: the k-th largest of the 2048
-  // values formed by every thread's largest and second largest key (each a distinct
-  // element of the chunk, so at least k keys lie at or above it), located to an
-  // 11-bit histogram bin and rounded down to that bin's lower edge
+  // ---- 1. row maximum and the lower bound t_lo: the k-th largest of the 4096
+  // values formed by every thread's four set maxima (set e holds the thread's keys
+  // 4g + e over its groups g), each a distinct element of the chunk, so at least k
+  // keys lie at or above it; located to an 11-bit histogram bin and rounded down to
+  // that bin's lower edge
   for (int b = tid; b < 2048; b += kThreads) hist[b] = 0;
-  uint32_t m1 = 0u, m2 = 0u;
+  uint32_t sm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    m2 = max(m2, min(m1, key[j]));
-    m1 = max(m1, key[j]);
-  }
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm[e] = max(sm[e], key[4 * g + e]);
+  const uint32_t m1 = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
   {
     // the smallest maximum over threads that hold a key (m1 = 0: none)
     const uint32_t wmax = wave_max_u32(m1), wmin = wave_min_u32(m1 ? m1 : 0xFFFFFFFFu);
@@ -350,14 +373,15 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     lo = min(lo, red_min[w]);
   }
   uint32_t tlo = kMinKey;
-  if (k <= 2 * kThreads && lo < M) {  // (uniform)
+  if (k <= 4 * kThreads && lo < M) {  // (uniform)
     // every counted value lies in [lo, M], so the bits above the highest bit in
     // which lo and M differ are common to all of them
     const int hi = 31 - __clz(lo ^ M);
     const int s = hi >= 10 ? hi - 10 : 0;
     const uint32_t dm = (1u << (hi - s + 1)) - 1u;
-    if (m1 >= lo) atomicAdd(&hist[(m1 >> s) & dm], 1);
-    if (m2 >= lo) atomicAdd(&hist[(m2 >> s) & dm], 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (sm[e] >= lo) atomicAdd(&hist[(sm[e] >> s) & dm], 1);
     __syncthreads();
     if (wave == 0) find_bin(hist, (int)dm + 1, k, info);
     __syncthreads();
@@ -368,16 +392,33 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
   }
   tlo = max(tlo, kMinKey);
 
-  // ---- 2. position-ordered count of the live keys; list them in LDS if they fit
+  // ---- 2. position-ordered count of the live keys; list them in LDS if they fit.
+  // A lane's count in a group is at most 4, so a wavefront's sum fits 10 bits:
+  // three groups share one prefix sum, in 10-bit fields.
+  constexpr int NW = (G + 2) / 3;
   uint32_t lex[G];  // exclusive prefix of this lane's live count in its (group, wave)
+  {
+    uint32_t packed[NW];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    uint32_t cnt = 0;
+    for (int w = 0; w < NW; ++w) packed[w] = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) cnt += key[4 * g + e] >= tlo ? 1u : 0u;
-    const uint32_t incl = wave_incl_scan(cnt);
-    lex[g] = incl - cnt;
-    if (lane == 63) tab[g * kWaves + wave] = incl;
+    for (int g = 0; g < G; ++g) {
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cnt += key[4 * g + e] >= tlo ? 1u : 0u;
+      packed[g / 3] += cnt << (10 * (g % 3));
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t incl = wave_incl_scan(packed[w]);
+#pragma unroll
+      for (int q = 0; q < 3 && 3 * w + q < G; ++q) {
+        const int g = 3 * w + q;
+        const uint32_t fi = (incl >> (10 * q)) & 1023u, fc = (packed[w] >> (10 * q)) & 1023u;
+        lex[g] = fi - fc;
+        if (lane == 63) tab[g * kWaves + wave] = fi;
+      }
+    }
   }
   __syncthreads();
   if (wave == 0) scan_table(tab, E, &total);
