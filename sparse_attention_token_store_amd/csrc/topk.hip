@@ -188,6 +188,30 @@ __device__ __forceinline__ void scan_table(uint32_t* tab, int E, uint32_t* total
   if (lane == 63) *total = incl;
 }
 
+// Every wavefront reads the per-(group, wave) counts tab[0..G*kWaves) itself and
+// takes the exclusive offsets of its own entries in position order (group-major,
+// then wave) and the total: no single-wave pass and no second barrier.  Entry
+// g*kWaves + w sits in lane 16*(g%4) + w of scan g/4 (kWaves = 16).
+template <int G>
+__device__ __forceinline__ void table_offsets(const uint32_t* tab, int wave, uint32_t (&off)[G], uint32_t& total) {
+  static_assert(kWaves == 16, "four groups per 64-entry scan");
+  constexpr int E = G * kWaves, J = (E + 63) / 64;
+  const int lane = lane_id();
+  uint32_t ex[J];
+  uint32_t base = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = 64 * j + lane;
+    const uint32_t x = i < E ? tab[i] : 0u;
+    const uint32_t inc = wave_incl_scan(x);
+    ex[j] = inc - x + base;
+    base += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  }
+  total = base;
+#pragma unroll
+  for (int g = 0; g < G; ++g) off[g] = (uint32_t)__builtin_amdgcn_readlane((int)ex[g >> 2], 16 * (g & 3) + wave);
+}
+
 // Physical cache slot of key position t of row r (the paged layout of the store:
 // logical block t / bs at offset t % bs, the block table naming the physical block),
 // or -1 when t is not a visible position of the row or a sequence or block id lies
@@ -421,14 +445,14 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     }
   }
   __syncthreads();
-  if (wave == 0) scan_table(tab, E, &total);
-  __syncthreads();
-  const int L = (int)total;
+  uint32_t goff[G], ltot;
+  table_offsets<G>(tab, __builtin_amdgcn_readfirstlane(wave), goff, ltot);
+  const int L = (int)ltot;
   const bool in_lds = L <= kListMax;
   if (in_lds) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      int at = (int)(tab[g * kWaves + wave] + lex[g]);
+      int at = (int)(goff[g] + lex[g]);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (key[4 * g + e] >= tlo) {  // (at < L <= kListMax)

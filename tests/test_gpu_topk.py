@@ -71,6 +71,30 @@ def test_topk_bit_exact(rows, n, k, kind):
                                                  np.setdiff1d(want[r], got[r])[:5])
 
 
+# Many rows of one chunk each, as chunked prefill makes them, with edge rows
+# throughout the batch (and at its end): empty, one key, exactly k, k + 1, every
+# score equal (more live keys than the list holds: the register passes) and NaNs.
+MANY_ROWS = [(1100, 36864, 1024), (700, 30000, 1024), (600, 22000, 512), (1100, 36864, 64)]
+
+
+@pytest.mark.parametrize("rows,n,k", MANY_ROWS)
+def test_topk_many_rows_bit_exact(rows, n, k):
+    x = gen.score_rows_for_topk(rows, n, kind="heavy", seed=rows + n + k)
+    rng = np.random.default_rng(rows + k)
+    lens = rng.integers(k + 2, n + 1, size=rows).astype(np.int64)
+    lens[[3, 300, rows - 1]] = 0
+    lens[[5, 301]] = 1
+    lens[[7, 302]] = k
+    lens[[9, rows - 2]] = k + 1
+    lens[[11, 303]] = n
+    x[13, :] = 2.5
+    x[15, rng.choice(n, 20, replace=False)] = np.nan
+    got = run_topk(x, lens, n, k)
+    want = O.topk(x, lens, k)
+    bad = [r for r in range(rows) if not np.array_equal(got[r], want[r])]
+    assert not bad, (len(bad), bad[:10])
+
+
 def test_topk_edge_lengths():
     k = 512
     lens = np.array([0, 1, k - 1, k, k + 1, 1023, 1024, 1025, 4096, 4097, 32768], np.int64)

@@ -70,7 +70,8 @@ def store_slot_of(wl):
     return table
 
 
-@pytest.mark.parametrize("cfg,scale", [(2, 0.05), (4, 0.01), (5, 0.02), (1, 1.0)])
+# (4, 1.0): all 4096 prefill rows
+@pytest.mark.parametrize("cfg,scale", [(2, 0.05), (4, 0.01), (5, 0.02), (1, 1.0), (4, 1.0)])
 def test_fused_slots(cfg, scale):
     wl = gen.config(cfg, scale=scale)
     g = GpuWorkload(wl)
