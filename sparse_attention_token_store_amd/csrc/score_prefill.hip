@@ -138,6 +138,37 @@ __device__ __forceinline__ Share load_share(const uint8_t* cache, int64_t num_bl
   return sh;
 }
 
+// Block size 64, fp8 keys, a stage wholly below the workgroup's longest row: the
+// stage's 256 keys fill four whole blocks, each thread's four code chunks come one
+// from each (chunk tid & 7 of key tid >> 3 of the block) and the scales of wave w
+// from block w & 3, so the four block ids are uniform (scalar loads) and a code
+// address is a uniform block base plus a per-thread offset that is the same in
+// every stage.
+__device__ __forceinline__ Share load_share_whole64(const uint8_t* cache, int64_t num_blocks,
+                                                    const int32_t* bt_row, int p0, int tid, int wave) {
+  constexpr uint32_t kBlockBytes = 64 * 132;
+  const uint32_t off = (uint32_t)(tid >> 3) * 128u + (uint32_t)(tid & 7) * 16u;
+  const uint8_t* base[4];
+  bool bad[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = bt_row[(p0 >> 6) + j];
+    bad[j] = e < 0 || (int64_t)e >= num_blocks;
+    base[j] = cache + (uint64_t)(bad[j] ? 0u : (uint32_t)e) * kBlockBytes;
+  }
+  Share sh;
+  sh.c0 = *reinterpret_cast<const uint4*>(base[0] + off);
+  sh.c1 = *reinterpret_cast<const uint4*>(base[1] + off);
+  sh.c2 = *reinterpret_cast<const uint4*>(base[2] + off);
+  sh.c3 = *reinterpret_cast<const uint4*>(base[3] + off);
+  const int j = wave & 3;
+  const uint8_t* sb = j == 0 ? base[0] : j == 1 ? base[1] : j == 2 ? base[2] : base[3];
+  const bool sbad = j == 0 ? bad[0] : j == 1 ? bad[1] : j == 2 ? bad[2] : bad[3];
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(sb + 64u * 128u + (uint32_t)(tid & 63) * 4u);
+  sh.scale = sbad ? 0x7FC00000u : v;  // a block id outside the pool: NaN scores
+  return sh;
+}
+
 template <bool kFp4>
 __device__ __forceinline__ void store_share(uint8_t* stage, const Share& sh, int tid) {
   if constexpr (kFp4) {
@@ -280,8 +311,19 @@ __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
         for (int p = k0 + lane; p < k1; p += 64) out[p] = -INFINITY;
       return;
     }
-    auto blocks = [&](int i) { return share_blocks<BS, kFp4>(bt_row, k0 + i * kStageKeys, n_max, tid); };
+    // (uniform copies: the scalar path below needs the compiler to know it)
+    const int n_max_u = __builtin_amdgcn_readfirstlane(n_max);
+    const int32_t* bt_row_u = block_table + (int64_t)__builtin_amdgcn_readfirstlane(s0) * max_blocks;
+    auto whole = [&](int i) {  // (uniform) stage i takes the scalar path
+      if constexpr (BS == 64 && !kFp4) return k0 + i * kStageKeys + kStageKeys <= n_max_u;
+      return false;
+    };
+    auto blocks = [&](int i) {
+      if (whole(i)) return ShareBlocks{0, 0, 0, 0, 0};  // (not used)
+      return share_blocks<BS, kFp4>(bt_row, k0 + i * kStageKeys, n_max, tid);
+    };
     auto share = [&](const ShareBlocks& e, int i) {
+      if (whole(i)) return load_share_whole64(cache, num_blocks, bt_row_u, k0 + i * kStageKeys, tid, wave);
       return load_share<BS, kFp4>(cache, num_blocks, e, k0 + i * kStageKeys, n_max, tid);
     };
     // Scores stage i from the staged copy st: groups of 16 keys, one 64-key store
