@@ -177,3 +177,39 @@ def test_prefill_ragged_row_count():
     g.quantise_q()
     got = gpu_scores(g, fp8_q=True)
     check_scores(got, oracle_scores(wl, OracleKeys(wl), q64=oracle_fp8_q(wl)), wl.row_len, RTOL["fp8"])
+
+
+def test_prefill_bad_blocks_in_whole_and_partial_stages():
+    # 64-token blocks: whole 256-key stages take their block ids by scalar loads,
+    # the last partial stage per lane; a negative id in a whole stage and an id past
+    # the pool in the partial stage each turn exactly their block's keys to NaN
+    wl = gen.config(4, scale=0.02, block_size=64)
+    seq = int(wl.row_seq[0])
+    n_max = int(wl.row_len.max())
+    last = (n_max - 1) // 64
+    # keys are split into 8 chunks of whole 64-key spans, each scored in 256-key
+    # stages; a stage is whole when it ends within the workgroup's longest row
+    ck = -(-(-(-n_max // 64)) // 8) * 64
+
+    def stage_end(p):
+        c = p // ck
+        return c * ck + (p - c * ck) // 256 * 256 + 256
+
+    for n_wg in (int(wl.row_len.min()), n_max):   # every workgroup's longest row lies in this range
+        assert stage_end(128) <= n_wg and stage_end(last * 64) > n_wg
+    bt = wl.block_table.copy()
+    bt[seq, 2] = -1
+    bt[seq, last] = wl.num_blocks + 7
+    g = GpuWorkload(wl, block_table=bt)
+    g.quantise_q()
+    got = gpu_scores(g, fp8_q=True)
+    bad = np.zeros(n_max, bool)
+    bad[128:192] = True
+    bad[last * 64:] = True
+    checked = 0
+    for r in range(wl.rows):
+        n = int(wl.row_len[r])
+        assert np.all(np.isnan(got[r, :n][bad[:n]])), r
+        assert np.all(np.isfinite(got[r, :n][~bad[:n]])), r
+        checked += int(n > last * 64)
+    assert checked > 0
