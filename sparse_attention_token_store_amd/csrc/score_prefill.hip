@@ -339,21 +339,28 @@ __global__ __launch_bounds__(kThreadsPf, 4) void score_prefill_kernel(
       float part[4];
 #pragma unroll
       for (int g = 0; g < kStageGroups; ++g) {
+        // A group's four MFMAs issue together and its epilogue follows them: the
+        // scheduling barriers keep the compiler from interleaving one group's
+        // epilogue with the next group's MFMAs (1165-1189 -> 1135-1137 us on the
+        // 4096 x 36,864 prefill; the four waves of a SIMD overlap the two instead).
         f32x4_t acc[4];
         if constexpr (kFp4) {
           const i32x8_t b = read_b4(st, g, lane);
           const int sb = scale_b4(reinterpret_cast<const uint32_t*>(st + kScaleOff4)[16 * g + (lane & 15)], lane);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)  // A: fp8 e4m3 at scale 2^0; B: fp4 e2m1 at its block scale
             acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sb);
         } else {
           const i32x8_t b = read_b(st, g, lane);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
             acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 qa[mt], b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
         }
+        __builtin_amdgcn_sched_barrier(0);
         part[g & 3] = group_part(acc, wq);
         if ((g & 3) == 3) {  // 64 keys done: lane l gets key l of the span, one store
           const int sp = g >> 2;
