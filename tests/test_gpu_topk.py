@@ -50,6 +50,11 @@ CASES = [
     (3, 60000, 256, "ties"),
     (3, 1000, 1, "normal"),
     (3, 1000, 7, "ties"),
+    # k past 1024 on one chunk: the bound from four set maxima per thread holds for
+    # k <= 4096 (k = 4097: no bound, every key live, the register passes)
+    (3, 36864, 3000, "heavy"),
+    (2, 36864, 4096, "ties"),
+    (2, 20000, 4097, "normal"),
     # more live keys than the kernel's LDS list holds: the register passes
     (2, 22000, 512, "equal"),
     (2, 36864, 1024, "equal"),
