@@ -179,9 +179,10 @@ def test_prefill_ragged_row_count():
     check_scores(got, oracle_scores(wl, OracleKeys(wl), q64=oracle_fp8_q(wl)), wl.row_len, RTOL["fp8"])
 
 
-def test_prefill_bad_blocks_in_whole_and_partial_stages():
-    # 64-token blocks: whole 256-key stages take their block ids by scalar loads,
-    # the last partial stage per lane; a negative id in a whole stage and an id past
+@pytest.mark.parametrize("kd", ["fp8", "fp4"])
+def test_prefill_bad_blocks_in_whole_and_partial_stages(kd):
+    # 64-token blocks: whole 256-key stages of fp8 keys take their block ids by scalar
+    # loads, the last partial stage (and MXFP4 keys) per lane; a negative id in a whole stage and an id past
     # the pool in the partial stage each turn exactly their block's keys to NaN
     wl = gen.config(4, scale=0.02, block_size=64)
     seq = int(wl.row_seq[0])
@@ -200,7 +201,7 @@ def test_prefill_bad_blocks_in_whole_and_partial_stages():
     bt = wl.block_table.copy()
     bt[seq, 2] = -1
     bt[seq, last] = wl.num_blocks + 7
-    g = GpuWorkload(wl, block_table=bt)
+    g = GpuWorkload(wl, block_table=bt, key_dtype=kd)
     g.quantise_q()
     got = gpu_scores(g, fp8_q=True)
     bad = np.zeros(n_max, bool)
