@@ -284,7 +284,14 @@ __global__ __launch_bounds__(kThreads) void topk_level_kernel(
     if constexpr (!kFirst || kVec) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const int l0 = li_of(g, 0), at = l0 < nc ? l0 : 0;
+        // The longest chunks (R = 36, one chunk per prefill row): l0 itself when
+        // l0 < nc (a multiple of 4 at most nc - 1), else the chunk's last whole four,
+        // with no compare mask kept alive (fewer spilled SGPRs: prefill 220 -> 213 us).
+        // Shorter chunks keep reading the first four for groups past the end, which
+        // measured faster there (decode_b32 rows 9.54 against 9.76 us, the 32,768-key
+        // levels of 1M-key rows 25.5 against 26.1 us).
+        const int l0 = li_of(g, 0);
+        const int at = R >= kMaxR ? min(l0, (nc - 1) & ~3) : (l0 < nc ? l0 : 0);
         uint4 v;
         if constexpr (kFirst)
           v = *reinterpret_cast<const uint4*>(scores + (int64_t)r * ld + base + at);
